@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident in HBM:
+    sparse_attn_pool_qk      block mean pooling of Q and K
+    sparse_attn_select_mask  pooled softmax, hybrid Top-k U Top-p mask and kept-block lists
+    sparse_attn_fwd_lists    block-sparse flash attention over the kept blocks
+on the Wan2.1-14B 720p-shaped workload (40 heads x 75600 tokens x 128, bf16, Bq=128, Bk=64,
+k_frac=0.03, p=0.9). Throughput is executed TFLOP/s: 4 d sum over kept (query block, key block)
+pairs of valid queries x valid keys, divided by the step time.
+
+Prints one JSON line. ``--gpus`` above 1 is refused: the library is a one-GPU kernel library.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan720p_traffic.json")
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_query_amd", "csrc", f)
+                for f in ("attn_fwd.hip", "sa_common.h")]
+
+
+def attn_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != attn_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def executed_flops(mask_cpu, n, bq, bk, d):
+    import numpy as np
+    nqb, nkb = mask_cpu.shape[-2:]
+    nq = np.array([min(bq, n - i * bq) for i in range(nqb)], dtype=np.float64)
+    nk = np.array([min(bk, n - j * bk) for j in range(nkb)], dtype=np.float64)
+    m = mask_cpu.astype(np.float64)
+    return float(4 * d * (m * nq[:, None] * nk[None, :]).sum())
+
+
+def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
+    """The float64 oracle on a bounded sample of the same workload, on the host cores."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    h = 0
+    q = x["q"][:, h:h + 1].double().numpy()
+    k = x["k"][:, h:h + 1].double().numpy()
+    v = x["v"][:, h:h + 1].double().numpy()
+    nqb = mask_cpu.shape[2]
+    t0 = time.perf_counter()
+    mask_o, _ = oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, 1.0 / math.sqrt(w.head_dim))
+    t_mask = time.perf_counter() - t0
+    blocks = sorted(set(np.linspace(0, nqb - 1, sample_blocks).round().astype(int).tolist()))
+    t0 = time.perf_counter()
+    oracle.masked_attention(q, k, v, mask_o, w.bq, w.bk, blocks=[(0, 0, i) for i in blocks])
+    t_attn = time.perf_counter() - t0
+    sub = np.zeros_like(mask_o)
+    sub[0, 0, blocks] = mask_o[0, 0, blocks]
+    flops = oracle.executed_flops(sub, w.tokens, w.bq, w.bk, w.head_dim)
+    t = t_attn + t_mask * len(blocks) / nqb
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.heads}: float64 mask oracle on all {nqb} query blocks ({t_mask:.2f} s, "
+                   f"prorated to the sample), masked-dense attention on {len(blocks)} evenly spaced query "
+                   f"blocks ({t_attn:.2f} s); executed FLOPs of those blocks / time"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "seconds": round(t_mask + t_attn, 2),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=240)
+    ap.add_argument("--sweep-out", default=None,
+                    help="also time the attention call on the density sweep and write JSON lines here")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this is a one-GPU kernel library. Heads are "
+              f"independent, so several GPUs would each run this same path on their share of heads.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import block_sparse_attention_query_amd as sa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    x = make_inputs(w)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (x["q"], x["k"], x["v"]))
+    B, H, N, d = q.shape
+    nqb, nkb = -(-N // w.bq), -(-N // w.bk)
+    qp = torch.empty((B, H, nqb, d), dtype=torch.float64, device=dev)
+    kp = torch.empty((B, H, nkb, d), dtype=torch.float64, device=dev)
+    sel = {"probs": torch.empty((B, H, nqb, nkb), dtype=torch.float64, device=dev),
+           "mask": torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=dev),
+           "kept_idx": torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=dev),
+           "kept_cnt": torch.empty((B, H, nqb), dtype=torch.int32, device=dev)}
+    o = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sa.pool_qk(q, k, w.bq, w.bk, out=(qp, kp))
+        if ev is not None:
+            ev[1].record()
+        sa.select_mask(qp, kp, w.k_frac, w.p, kept_lists=True, out=sel)
+        if ev is not None:
+            ev[2].record()
+        sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, out=o)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mask_cpu = sel["mask"].cpu().numpy()
+    flops = executed_flops(mask_cpu, N, w.bq, w.bk, d)
+    density = float(mask_cpu.mean())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    pool_ms, select_ms, attn_ms = (float(v) for v in per.mean(axis=0))
+
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": "sparse attention fwd TFLOP/s (executed) + ms/call at 95% sparsity; % bf16 MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: Wan2.1-14B 720p-shaped latent grid 21x45x80",
+                   "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq, "bk": w.bk,
+                   "k_frac": w.k_frac, "p": w.p, "kept_block_density": round(density, 5),
+                   "block_sparsity": round(1 - density, 5), "executed_tflop_per_step": round(flops / 1e12, 4),
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_call": {"pool_qk": round(pool_ms, 4), "select_mask": round(select_ms, 4),
+                        "fwd_lists": round(attn_ms, 4)},
+        "fwd_tflops": round(attn_tflops, 2),
+        "fwd_pct_bf16_peak": round(100 * attn_tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": "attn_fwd_kernel<bf16, 128, 128>", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "pool_gbs": round(2 * B * H * N * d * q.element_size() / (pool_ms * 1e-3) / 1e9, 1),
+        "input_generation_s": round(gen_s, 1),
+    }
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            for kf in w.sweep or (1.0, 0.5, 0.25, 0.10, 0.05, 0.03):
+                s2 = sa.select_mask(qp, kp, kf, 0.0, kept_lists=True)
+                for _ in range(2):
+                    sa.fwd_lists(q, k, v, s2["kept_idx"], s2["kept_cnt"], w.bq, w.bk, out=o)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                a.record()
+                for _ in range(5):
+                    sa.fwd_lists(q, k, v, s2["kept_idx"], s2["kept_cnt"], w.bq, w.bk, out=o)
+                b.record()
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / 5
+                m2 = s2["mask"].cpu().numpy()
+                fl = executed_flops(m2, N, w.bq, w.bk, d)
+                rec = {"k_frac": kf, "p": 0.0, "density": float(m2.mean()), "fwd_ms": ms,
+                       "fwd_tflops": fl / (ms * 1e-3) / 1e12}
+                f.write(json.dumps(rec) + "\n")
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, mask_cpu, args.cpu_sample_blocks)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,167 @@
+"""Block-sparse attention in the SpargeAttention2 form for MI355X (gfx950).
+
+Thin torch binding over the C ABI in ``include/sparse_attn.h``: it checks tensor placement and
+layout, allocates outputs with torch, and passes raw device pointers and torch's current HIP
+stream. Every step of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and a missing library raises.
+
+    q_pool, k_pool = pool_qk(q, k, bq, bk)
+    sel = select_mask(q_pool, k_pool, k_frac, p)          # probs, mask (+ kept lists)
+    o = fwd(q, k, v, sel["mask"], bq, bk)
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import SA_BF16, SA_F32, SparseAttnError  # noqa: F401
+
+__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "topk_count", "sparse_attention",
+           "SparseAttnError"]
+
+_DTYPES = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_qkv(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.dim() != 4:
+            raise ValueError("expected [B, H, N, d] tensors")
+        if t.dtype != ts[0].dtype or t.shape != ts[0].shape or t.device != ts[0].device:
+            raise ValueError("q, k, v must share dtype, shape and device")
+    if ts[0].dtype not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+
+
+def _nblocks(n: int, b: int) -> int:
+    return -(-n // b)
+
+
+def topk_count(k_frac: float, nkb: int) -> int:
+    """Top-k size the library uses for a kept fraction (host arithmetic of the C ABI)."""
+    return int(_lib.lib().sparse_attn_topk_count(float(k_frac), int(nkb)))
+
+
+def _check_out(t: torch.Tensor, shape, dtype, device) -> torch.Tensor:
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"output buffer must be a contiguous {dtype} {list(shape)} tensor on {device}")
+    return t
+
+
+def pool_qk(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, out=None):
+    """Mean-pooled Q over blocks of ``bq`` and K over blocks of ``bk`` (float64 outputs).
+
+    ``out`` may pass preallocated ``(q_pool, k_pool)`` buffers.
+    """
+    _check_qkv(q, k)
+    B, H, N, d = q.shape
+    qshape, kshape = (B, H, _nblocks(N, bq), d), (B, H, _nblocks(N, bk), d)
+    if out is None:
+        qp = torch.empty(qshape, dtype=torch.float64, device=q.device)
+        kp = torch.empty(kshape, dtype=torch.float64, device=q.device)
+    else:
+        qp = _check_out(out[0], qshape, torch.float64, q.device)
+        kp = _check_out(out[1], kshape, torch.float64, q.device)
+    _lib.check(_lib.lib().sparse_attn_pool_qk(q.data_ptr(), k.data_ptr(), _DTYPES[q.dtype], B, H, N, d, bq, bk,
+                                              qp.data_ptr(), kp.data_ptr(), _stream(q)))
+    return qp, kp
+
+
+def select_mask(q_pool: torch.Tensor, k_pool: torch.Tensor, k_frac: float, p: float, scale: float | None = None,
+                kept_lists: bool = False, out: dict | None = None):
+    """Pooled probabilities and the hybrid Top-k U Top-p block mask.
+
+    Returns a dict with ``probs`` (float64 ``[B,H,nQB,nKB]``), ``mask`` (uint8) and, when
+    ``kept_lists`` is set, ``kept_idx`` / ``kept_cnt`` (int32). ``out`` may pass a dict of
+    preallocated buffers under the same keys.
+    """
+    for t in (q_pool, k_pool):
+        if not t.is_cuda or t.dtype != torch.float64 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("pooled tensors must be contiguous float64 [B, H, n, d] GPU tensors")
+    B, H, nqb, d = q_pool.shape
+    nkb = k_pool.shape[2]
+    if k_pool.shape[:2] != (B, H) or k_pool.shape[3] != d:
+        raise ValueError("q_pool and k_pool shapes disagree")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dev = q_pool.device
+    want = {"probs": ((B, H, nqb, nkb), torch.float64), "mask": ((B, H, nqb, nkb), torch.uint8)}
+    if kept_lists:
+        want["kept_idx"] = ((B, H, nqb, nkb), torch.int32)
+        want["kept_cnt"] = ((B, H, nqb), torch.int32)
+    given = out or {}
+    out = {name: (_check_out(given[name], shp, dt, dev) if name in given else torch.empty(shp, dtype=dt, device=dev))
+           for name, (shp, dt) in want.items()}
+    probs, mask = out["probs"], out["mask"]
+    idx_ptr = cnt_ptr = None
+    if kept_lists:
+        idx_ptr, cnt_ptr = out["kept_idx"].data_ptr(), out["kept_cnt"].data_ptr()
+    _lib.check(_lib.lib().sparse_attn_select_mask(q_pool.data_ptr(), k_pool.data_ptr(), B, H, nqb, nkb, d, scale,
+                                                  float(k_frac), float(p), probs.data_ptr(), mask.data_ptr(),
+                                                  idx_ptr, cnt_ptr, _stream(q_pool)))
+    return out
+
+
+def fwd_workspace_size(B: int, H: int, N: int, bq: int, bk: int = 64) -> int:
+    return int(_lib.lib().sparse_attn_fwd_workspace_size(B, H, N, bq, bk))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, bq: int, bk: int = 64,
+        scale: float | None = None, return_lse: bool = False, workspace: torch.Tensor | None = None,
+        out: torch.Tensor | None = None):
+    """Block-sparse attention of each query block over its kept key blocks."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (B, H, nqb, nkb) or not mask.is_contiguous() \
+            or mask.device != q.device:
+        raise ValueError(f"mask must be a contiguous uint8 [{B}, {H}, {nqb}, {nkb}] tensor on {q.device}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ws_bytes = fwd_workspace_size(B, H, N, bq, bk)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.check(_lib.lib().sparse_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype],
+                                          mask.data_ptr(), B, H, N, d, bq, bk, scale, o.data_ptr(),
+                                          None if lse is None else lse.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor, kept_cnt: torch.Tensor,
+              bq: int, bk: int = 64, scale: float | None = None, return_lse: bool = False,
+              out: torch.Tensor | None = None):
+    """Block-sparse attention from kept-block lists (as written by ``select_mask(kept_lists=True)``)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    if kept_idx.dtype != torch.int32 or tuple(kept_idx.shape) != (B, H, nqb, nkb) or not kept_idx.is_contiguous():
+        raise ValueError(f"kept_idx must be a contiguous int32 [{B}, {H}, {nqb}, {nkb}] tensor")
+    if kept_cnt.dtype != torch.int32 or tuple(kept_cnt.shape) != (B, H, nqb) or not kept_cnt.is_contiguous():
+        raise ValueError(f"kept_cnt must be a contiguous int32 [{B}, {H}, {nqb}] tensor")
+    if kept_idx.device != q.device or kept_cnt.device != q.device:
+        raise ValueError("kept lists must be on the device of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.check(_lib.lib().sparse_attn_fwd_lists(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype],
+                                                kept_idx.data_ptr(), kept_cnt.data_ptr(), B, H, N, d, bq, bk, scale,
+                                                o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def sparse_attention(q, k, v, bq: int, bk: int, k_frac: float, p: float, scale: float | None = None):
+    """Pooling, mask selection and sparse attention in sequence; returns (o, mask)."""
+    qp, kp = pool_qk(q, k, bq, bk)
+    sel = select_mask(qp, kp, k_frac, p, scale)
+    return fwd(q, k, v, sel["mask"], bq, bk, scale), sel["mask"]

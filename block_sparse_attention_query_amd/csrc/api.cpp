@@ -1,0 +1,187 @@
+// C ABI entry points: host-side argument checks, shape arithmetic and kernel launches.
+// Every check runs before the first HIP call, so invalid arguments enqueue nothing (and can be
+// exercised on a machine without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+hipError_t launch_pool(const void* q, const void* k, int dtype, int BH, int N, int d, int Bq, int Bk, double* qp,
+                       double* kp, hipStream_t stream);
+hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, int nkb, int d, double scale, int k,
+                         double p, double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt,
+                         hipStream_t stream);
+hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
+hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
+                       const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
+                       hipStream_t stream);
+}  // namespace sa
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shapes shared by the calls; products are checked to stay within 32-bit grid limits.
+int check_shape(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return fail(SA_ERR_INVALID_ARG, "B, H, N and d must be positive");
+  if ((long long)B * H > 65535) return fail(SA_ERR_UNSUPPORTED, "B*H = %lld exceeds 65535", (long long)B * H);
+  if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+  return SA_OK;
+}
+
+int check_dtype(int dtype) {
+  if (dtype != SA_BF16 && dtype != SA_F32) return fail(SA_ERR_UNSUPPORTED, "dtype %d not SA_BF16 or SA_F32", dtype);
+  return SA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_topk_count(double k_frac, int nkb) {
+  if (!(k_frac >= 0.0 && k_frac <= 1.0) || nkb <= 0) return -1;
+  double x = ceil(k_frac * (double)nkb - 1e-9);
+  if (x < 0.0) x = 0.0;
+  if (x > (double)nkb) x = (double)nkb;
+  return (int)x;
+}
+
+const char* sparse_attn_error_string(int code) {
+  switch (code) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_HIP: return "HIP error";
+    default: return "unknown error code";
+  }
+}
+
+const char* sparse_attn_last_error(void) { return g_last_error; }
+
+int sparse_attn_pool_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d, int Bq, int Bk,
+                        double* q_pool, double* k_pool, void* stream) {
+  if (!q || !k || !q_pool || !k_pool) return fail(SA_ERR_INVALID_ARG, "pool_qk: null pointer");
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((Bq != 64 && Bq != 128) || (Bk != 64 && Bk != 128))
+    return fail(SA_ERR_UNSUPPORTED, "pool_qk: block sizes Bq=%d Bk=%d not in {64, 128}", Bq, Bk);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_pool) || !aligned16(k_pool))
+    return fail(SA_ERR_INVALID_ARG, "pool_qk: pointers must be 16-byte aligned");
+  const long long blocks = (long long)B * H * (cdiv(N, Bq) + cdiv(N, Bk));
+  if (blocks > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "pool_qk: too many blocks");
+  return hip_status(sa::launch_pool(q, k, dtype, B * H, N, d, Bq, Bk, q_pool, k_pool,
+                                    static_cast<hipStream_t>(stream)),
+                    "pool_qk launch");
+}
+
+int sparse_attn_select_mask(const double* q_pool, const double* k_pool, int B, int H, int nqb, int nkb, int d,
+                            double scale, double k_frac, double p, double* probs, uint8_t* mask, int32_t* kept_idx,
+                            int32_t* kept_cnt, void* stream) {
+  if (!q_pool || !k_pool || !probs || !mask) return fail(SA_ERR_INVALID_ARG, "select_mask: null pointer");
+  if ((kept_idx == nullptr) != (kept_cnt == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "select_mask: kept_idx and kept_cnt must both be given or both be NULL");
+  if (nqb <= 0 || nkb <= 0) return fail(SA_ERR_INVALID_ARG, "select_mask: nqb and nkb must be positive");
+  int rc = check_shape(B, H, 1, d);
+  if (rc) return rc;
+  if (nkb > SA_MAX_NKB) return fail(SA_ERR_UNSUPPORTED, "select_mask: nkb=%d exceeds %d", nkb, SA_MAX_NKB);
+  if ((long long)B * H * nqb > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "select_mask: too many rows");
+  if ((cdiv(nqb, 64)) > 65535) return fail(SA_ERR_UNSUPPORTED, "select_mask: nqb too large");
+  if (!(scale > 0.0) || !isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "select_mask: scale must be finite and > 0");
+  if (!(k_frac >= 0.0 && k_frac <= 1.0)) return fail(SA_ERR_INVALID_ARG, "select_mask: k_frac must lie in [0, 1]");
+  if (!(p >= 0.0 && p <= 1.0)) return fail(SA_ERR_INVALID_ARG, "select_mask: p must lie in [0, 1]");
+  const int k = sparse_attn_topk_count(k_frac, nkb);
+  return hip_status(sa::launch_select(q_pool, k_pool, B * H, nqb, nkb, d, scale, k, p, probs, mask, kept_idx,
+                                      kept_cnt, static_cast<hipStream_t>(stream)),
+                    "select_mask launch");
+}
+
+size_t sparse_attn_fwd_workspace_size(int B, int H, int N, int Bq, int Bk) {
+  if (B <= 0 || H <= 0 || N <= 0 || Bq <= 0 || Bk <= 0) return 0;
+  const size_t rows = (size_t)B * H * cdiv(N, Bq);
+  const size_t nkb = (size_t)cdiv(N, Bk);
+  return align_up(rows * nkb * sizeof(int32_t)) + align_up(rows * sizeof(int32_t));
+}
+
+namespace {
+int check_fwd_common(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d, int Bq,
+                     int Bk, double scale, const void* o) {
+  if (!q || !k || !v || !o) return fail(SA_ERR_INVALID_ARG, "fwd: null pointer");
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if ((Bq != 64 && Bq != 128) || Bk != 64)
+    return fail(SA_ERR_UNSUPPORTED, "fwd: block sizes Bq=%d Bk=%d (need Bq in {64,128}, Bk = 64)", Bq, Bk);
+  if (!(scale > 0.0) || !isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "fwd: scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SA_ERR_INVALID_ARG, "fwd: q, k, v and o must be 16-byte aligned");
+  if ((long long)B * H * cdiv(N, Bq) > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "fwd: too many query blocks");
+  return SA_OK;
+}
+}  // namespace
+
+int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                          const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, double scale, void* o,
+                          float* lse, void* stream) {
+  if (!kept_idx || !kept_cnt) return fail(SA_ERR_INVALID_ARG, "fwd_lists: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, o);
+  if (rc) return rc;
+  return hip_status(sa::launch_attn(q, k, v, dtype, kept_idx, kept_cnt, B * H, N, d, Bq, scale, o, lse,
+                                    static_cast<hipStream_t>(stream)),
+                    "fwd_lists: attention launch");
+}
+
+int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask, int B, int H, int N,
+                    int d, int Bq, int Bk, double scale, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!mask || !workspace) return fail(SA_ERR_INVALID_ARG, "fwd: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, o);
+  if (rc) return rc;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(SA_ERR_INVALID_ARG, "fwd: workspace must be 256-byte aligned");
+  const size_t need = sparse_attn_fwd_workspace_size(B, H, N, Bq, Bk);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_INVALID_ARG, "fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  const int nqb = cdiv(N, Bq), nkb = cdiv(N, Bk);
+  const long long rows = (long long)B * H * nqb;
+  int32_t* kidx = static_cast<int32_t*>(workspace);
+  int32_t* kcnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             align_up((size_t)rows * nkb * sizeof(int32_t)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_status(sa::launch_compact(mask, (int)rows, nkb, kidx, kcnt, s), "fwd: compaction launch");
+  if (rc) return rc;
+  return hip_status(sa::launch_attn(q, k, v, dtype, kidx, kcnt, B * H, N, d, Bq, scale, o, lse, s),
+                    "fwd: attention launch");
+}
+
+}  // extern "C"

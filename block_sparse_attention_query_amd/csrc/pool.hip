@@ -1,0 +1,91 @@
+// Block mean pooling of Q and K (gfx950).
+//
+// Consecutive tokens form a block that is represented by one pooled vector (Sparse VideoGen2
+// page, section "1. 問題定義"); the mean over the block's valid tokens is taken. The kernel is
+// HBM-bound: every Q and K element is read exactly once with 16-byte coalesced loads, summed in
+// float64 (exact for bf16 inputs), reduced across row groups through LDS in a fixed order, and
+// divided once by the valid token count.
+#include "sa_common.h"
+
+namespace sa {
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, const void* __restrict__ k,
+                                                   int BH, int N, int Bq, int Bk, int nqb, int nkb,
+                                                   double* __restrict__ qp, double* __restrict__ kp) {
+  constexpr int ES = DT == kBF16 ? 2 : 4;  // bytes per element
+  constexpr int EPV = 16 / ES;             // elements per 16-byte vector
+  constexpr int VPR = D / EPV;             // vectors per token row
+  constexpr int RG = 256 / VPR;            // token rows covered by one pass of the workgroup
+  __shared__ double red[RG][D + 1];
+
+  int blk = blockIdx.x;
+  const char* src;
+  double* dst;
+  int bsz, bh, i;
+  if (blk < BH * nqb) {
+    bh = blk / nqb;
+    i = blk - bh * nqb;
+    src = static_cast<const char*>(q);
+    bsz = Bq;
+    dst = qp + (size_t)blk * D;
+  } else {
+    blk -= BH * nqb;
+    bh = blk / nkb;
+    i = blk - bh * nkb;
+    src = static_cast<const char*>(k);
+    bsz = Bk;
+    dst = kp + (size_t)blk * D;
+  }
+  const int row0 = i * bsz;
+  const int nvalid = min(bsz, N - row0);
+  const uint4* base = reinterpret_cast<const uint4*>(src + ((size_t)bh * N + row0) * (size_t)(D * ES));
+  const int c = threadIdx.x % VPR;
+  const int r0 = threadIdx.x / VPR;
+
+  double acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+#pragma unroll 8
+  for (int r = r0; r < nvalid; r += RG) {
+    const uint4 v = base[(size_t)r * VPR + c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(w[e]);
+        acc[2 * e + 1] += (double)bf16_hi(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(w[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) red[r0][c * EPV + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+    for (int g = 0; g < RG; ++g) s += red[g][threadIdx.x];
+    dst[threadIdx.x] = s / (double)nvalid;
+  }
+}
+
+hipError_t launch_pool(const void* q, const void* k, int dtype, int BH, int N, int d, int Bq, int Bk,
+                       double* qp, double* kp, hipStream_t stream) {
+  const int nqb = (N + Bq - 1) / Bq;
+  const int nkb = (N + Bk - 1) / Bk;
+  const dim3 grid((unsigned)(BH * (nqb + nkb)));
+  const dim3 block(256);
+  if (dtype == kBF16 && d == 128)
+    hipLaunchKernelGGL((pool_kernel<kBF16, 128>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  else if (dtype == kBF16 && d == 64)
+    hipLaunchKernelGGL((pool_kernel<kBF16, 64>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  else if (dtype == kF32 && d == 128)
+    hipLaunchKernelGGL((pool_kernel<kF32, 128>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  else
+    hipLaunchKernelGGL((pool_kernel<kF32, 64>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  return hipGetLastError();
+}
+
+}  // namespace sa

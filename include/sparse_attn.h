@@ -1,0 +1,148 @@
+/*
+ * sparse_attn.h - C ABI of the MI355X (gfx950) block-sparse attention library.
+ *
+ * Training-free block-sparse softmax attention in the SpargeAttention2 form:
+ *   1. sparse_attn_pool_qk      mean-pool Q and K over consecutive token blocks;
+ *   2. sparse_attn_select_mask  pooled scores, a softmax per query block, and the hybrid
+ *                               Top-k U Top-p block mask;
+ *   3. sparse_attn_fwd          flash-style attention of every query block over its kept key
+ *                               blocks only.
+ *
+ * Pages the operations follow:
+ *   [SA2]  "SpargeAttention2とは？Top-k+Top-pハイブリッドマスキングでビデオ生成を16.2倍高速化"
+ *          (ai-papers.net), sections "Top-kとTop-pの限界を解剖する" and
+ *          "ハイブリッドマスキングと蒸留微調整".
+ *   [SVG2] "Sparse VideoGen2: Accelerate Video Generation with Sparse Attention via
+ *          Semantic-Aware Permutation" (gist.science), sections "1. 問題定義" and "2. 手法" B, C.
+ *   [SPR]  "Partition the Support, Reconstruct the Residual: Training-Free Sparse Attention for
+ *          Video Generation and World Models" (physicalainews.jp), original abstract.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are device memory on the current HIP device; all tensors are
+ *     dense and contiguous in the stated layout; the caller allocates and owns every buffer.
+ *   - The library never allocates, frees or synchronises. Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*, NULL = the null stream) and runs asynchronously.
+ *   - Arguments are checked on the host before anything is enqueued. A non-zero return means
+ *     nothing was enqueued, except SA_ERR_HIP, which reports a failed launch.
+ *     sparse_attn_last_error() then holds a message for the calling thread.
+ *   - NaN or Inf inside the tensors is not checked; it propagates.
+ *   - Shapes: B batch, H heads, N tokens, d head dim, Bq / Bk query / key block sizes,
+ *     nQB = ceil(N / Bq), nKB = ceil(N / Bk). The last block of each may be partial; pooling
+ *     averages its valid tokens and padded keys never take part in attention.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SA_OK 0
+#define SA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, value out of range   */
+#define SA_ERR_UNSUPPORTED (-2) /* d, Bq, Bk, dtype or nKB outside the instantiated set    */
+#define SA_ERR_HIP (-3)         /* a HIP launch failed; the HIP message is kept          */
+
+/* Element types of Q, K, V and O. Both are computed with bf16 MFMA operands and fp32
+ * accumulation; fp32 tiles are rounded to bf16 (nearest-even) when staged. */
+#define SA_BF16 0
+#define SA_F32 1
+
+/* Supported values (others return SA_ERR_UNSUPPORTED): d in {64, 128}; Bq in {64, 128};
+ * Bk = 64 for sparse_attn_fwd (pooling accepts Bq, Bk in {64, 128}); nKB <= 8192. */
+#define SA_MAX_NKB 8192
+
+/*
+ * Block mean pooling of Q and K ([SVG2] "1. 問題定義": consecutive tokens grouped into blocks,
+ * each represented by a pooled vector; mean pooling).
+ *
+ *   q, k      device, [B, H, N, d] of `dtype`.
+ *   q_pool    device out, [B, H, nQB, d] float64: q_pool[b,h,i,:] = mean of Q rows
+ *             i*Bq .. min(N, (i+1)*Bq) - 1.
+ *   k_pool    device out, [B, H, nKB, d] float64, the same over key blocks of Bk.
+ * Sums are accumulated in float64, so the means are exact up to the final division.
+ */
+int sparse_attn_pool_qk(const void* q, const void* k, int dtype, int B, int H, int N, int d,
+                        int Bq, int Bk, double* q_pool, double* k_pool, void* stream);
+
+/*
+ * Pooled probability pattern and hybrid block mask ([SA2] "Top-kとTop-pの限界を解剖する",
+ * "ハイブリッドマスキングと蒸留微調整"; [SVG2] "2. 手法" B).
+ *
+ *   q_pool, k_pool   device, [B, H, nqb, d] and [B, H, nkb, d] float64 (from pool_qk).
+ *   scale            score scale, normally 1/sqrt(d).
+ *   k_frac           Top-k fraction in [0, 1]; k = min(nkb, ceil(k_frac * nkb - 1e-9)).
+ *   p                Top-p mass in [0, 1]; keeps the shortest prefix of the descending order
+ *                    whose running sum is >= p (p = 0 keeps none by Top-p).
+ *   probs            device out, [B, H, nqb, nkb] float64: softmax over j of
+ *                    scale * <q_pool[b,h,i], k_pool[b,h,j]>.
+ *   mask             device out, [B, H, nqb, nkb] uint8, 1 = keep. Row i keeps the first
+ *                    max(k, m*) blocks of the order "descending probability, lower index first
+ *                    on equality", m* being the Top-p prefix length.
+ *   kept_idx         device out or NULL, [B, H, nqb, nkb] int32: per row the kept block
+ *                    indices in ascending order in the first kept_cnt entries (rest unwritten).
+ *   kept_cnt         device out or NULL (both or neither), [B, H, nqb] int32.
+ * Scores, softmax and running sums are float64.
+ */
+int sparse_attn_select_mask(const double* q_pool, const double* k_pool, int B, int H, int nqb,
+                            int nkb, int d, double scale, double k_frac, double p, double* probs,
+                            uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/* Bytes of device workspace sparse_attn_fwd needs for these shapes (kept-block lists and
+ * per-row counts, 256-byte aligned). Returns 0 for invalid shapes. */
+size_t sparse_attn_fwd_workspace_size(int B, int H, int N, int Bq, int Bk);
+
+/*
+ * Block-sparse attention forward ([SVG2] "2. 手法" C: scattered K/V blocks are loaded, the
+ * contiguous query block is computed densely; [SPR] abstract: queries sharing a block route
+ * share its key support).
+ *
+ *   q, k, v     device, [B, H, N, d] of `dtype`.
+ *   mask        device, [B, H, nQB, nKB] uint8, any 0/1 pattern (from select_mask, all ones for
+ *               dense attention, or a caller's own).
+ *   scale       softmax scale, normally 1/sqrt(d).
+ *   o           device out, [B, H, N, d] of `dtype`: for every query t of block i,
+ *               O[t] = sum_u softmax_u(scale * Q[t].K[u]) V[u] over the keys u < N of the kept
+ *               blocks of row i. A row with no kept block gives O = 0.
+ *   lse         device out or NULL, [B, H, N] float32: natural-log log-sum-exp of the scaled
+ *               scores over the same keys (-inf for an empty row).
+ *   workspace   device scratch of at least sparse_attn_fwd_workspace_size() bytes, 256-byte
+ *               aligned; overwritten.
+ * The mask is compacted into ascending kept-block lists in the workspace, then one workgroup
+ * per (b, h, query block) walks its list with bf16 MFMA and an fp32 online softmax.
+ */
+int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
+                    int B, int H, int N, int d, int Bq, int Bk, double scale, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same attention from kept-block lists instead of a mask (the kept_idx / kept_cnt that
+ * sparse_attn_select_mask can write), skipping the compaction step.
+ *
+ *   kept_idx    device, [B, H, nQB, nKB] int32: row r walks kept_idx[r][0 .. kept_cnt[r]-1].
+ *   kept_cnt    device, [B, H, nQB] int32.
+ * Entries are expected ascending in [0, nKB) and counts in [0, nKB]. The kernel clamps counts
+ * to that range and never reads K/V outside [0, N); other bad entries give unspecified values.
+ * The remaining arguments are those of sparse_attn_fwd.
+ */
+int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                          const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, double scale,
+                          void* o, float* lse, void* stream);
+
+/* Host helper: the Top-k size for a fraction, as select_mask computes it (-1 if invalid). */
+int sparse_attn_topk_count(double k_frac, int nkb);
+
+/* Static text for a return code. */
+const char* sparse_attn_error_string(int code);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

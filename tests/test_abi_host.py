@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every declared symbol,
+and rejects invalid arguments with the documented codes before touching the GPU."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+from block_sparse_attention_query_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsparse_attn.so not built")
+
+# Fake device addresses: never dereferenced because every call below fails validation first.
+P = 1 << 20      # 256-byte aligned
+P_ODD = P + 8    # not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 8
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_error_strings():
+    lib = _lib.lib()
+    assert lib.sparse_attn_error_string(0) == b"ok"
+    for c in (-1, -2, -3):
+        assert lib.sparse_attn_error_string(c)
+    assert lib.sparse_attn_error_string(17) == b"unknown error code"
+
+
+def test_topk_count_matches_oracle_rule():
+    lib = _lib.lib()
+    for nkb in (1, 7, 16, 256, 512, 1182, 8192):
+        for k_frac in (0.0, 0.01, 0.03, 0.05, 0.1, 0.25, 0.3, 1 / 3, 0.5, 0.6, 0.9, 0.999, 1.0):
+            assert lib.sparse_attn_topk_count(k_frac, nkb) == oracle.topk_count(k_frac, nkb), (k_frac, nkb)
+    assert lib.sparse_attn_topk_count(-0.1, 10) == -1
+    assert lib.sparse_attn_topk_count(1.5, 10) == -1
+    assert lib.sparse_attn_topk_count(float("nan"), 10) == -1
+
+
+def test_workspace_size():
+    lib = _lib.lib()
+    rows, nkb = 40 * 591, 1182
+    want = math.ceil(rows * nkb * 4 / 256) * 256 + math.ceil(rows * 4 / 256) * 256
+    assert lib.sparse_attn_fwd_workspace_size(1, 40, 75600, 128, 64) == want
+    assert lib.sparse_attn_fwd_workspace_size(0, 40, 75600, 128, 64) == 0
+
+
+def _pool(**kw):
+    a = dict(q=P, k=P, dtype=0, B=1, H=2, N=1024, d=64, Bq=64, Bk=64, qp=P, kp=P, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_pool_qk(*a.values())
+
+
+def _select(**kw):
+    a = dict(qp=P, kp=P, B=1, H=2, nqb=16, nkb=16, d=64, scale=0.125, k_frac=0.25, p=0.6, probs=P, mask=P,
+             idx=None, cnt=None, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_select_mask(*a.values())
+
+
+def _fwd(**kw):
+    ws = _lib.lib().sparse_attn_fwd_workspace_size(1, 2, 1024, 64, 64)
+    a = dict(q=P, k=P, v=P, dtype=0, mask=P, B=1, H=2, N=1024, d=64, Bq=64, Bk=64, scale=0.125, o=P, lse=None,
+             ws=P, ws_bytes=ws, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kp=None), -1), (dict(N=0), -1), (dict(B=-1), -1),
+    (dict(d=96), -2), (dict(Bq=32), -2), (dict(Bk=256), -2), (dict(dtype=5), -2), (dict(q=P_ODD), -1),
+    (dict(B=300, H=300), -2),
+])
+def test_pool_rejects(kw, code):
+    assert _pool(**kw) == code
+    assert _lib.lib().sparse_attn_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qp=None), -1), (dict(mask=None), -1), (dict(probs=None), -1), (dict(idx=P), -1), (dict(cnt=P), -1),
+    (dict(nkb=0), -1), (dict(d=32), -2), (dict(nkb=8193), -2), (dict(k_frac=-0.01), -1), (dict(k_frac=1.01), -1),
+    (dict(p=float("nan")), -1), (dict(p=1.5), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1),
+])
+def test_select_rejects(kw, code):
+    assert _select(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), -1), (dict(mask=None), -1), (dict(ws=None), -1), (dict(o=None), -1), (dict(N=-5), -1),
+    (dict(d=80), -2), (dict(Bk=128), -2), (dict(Bq=256), -2), (dict(dtype=2), -2), (dict(ws_bytes=100), -1),
+    (dict(ws=P + 16), -1), (dict(o=P_ODD), -1), (dict(scale=-1.0), -1),
+])
+def test_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def _fwd_lists(**kw):
+    a = dict(q=P, k=P, v=P, dtype=0, idx=P, cnt=P, B=1, H=2, N=1024, d=64, Bq=64, Bk=64, scale=0.125, o=P,
+             lse=None, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_fwd_lists(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), -1), (dict(cnt=None), -1), (dict(q=None), -1), (dict(d=48), -2), (dict(Bk=32), -2),
+    (dict(k=P_ODD), -1), (dict(scale=float("nan")), -1), (dict(H=0), -1),
+])
+def test_fwd_lists_rejects(kw, code):
+    assert _fwd_lists(**kw) == code
+
+
+def test_last_error_names_the_problem():
+    assert _fwd(ws_bytes=100) == -1
+    msg = _lib.lib().sparse_attn_last_error().decode()
+    assert "workspace" in msg and "100" in msg
+    with pytest.raises(_lib.SparseAttnError) as ei:
+        _lib.check(_fwd(d=80))
+    assert ei.value.code == -2 and "80" in str(ei.value)
