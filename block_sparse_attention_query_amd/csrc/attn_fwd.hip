@@ -154,7 +154,7 @@ __device__ __forceinline__ void stage_store(char* __restrict__ buf, const uint4 
 }
 
 template <int DT, int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(BQ * 2) void attn_fwd_staged_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
     void* __restrict__ o, float* __restrict__ lse) {
@@ -310,6 +310,250 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 kernel
+
+// bf16 inputs need no conversion on the way into LDS, so K and V blocks are copied HBM -> LDS by
+// global_load_lds_dwordx4 (lane i of an instruction fills bytes 16 i .. 16 i + 15 of a 1 KiB
+// stretch) and never occupy VGPRs. Both tiles keep their natural [key][channel] layout:
+//  - K fragments (A operand of S^T = K Q^T) are 16-byte ds_read_b128 of one key row;
+//  - V^T fragments (A operand of O^T += V^T P^T) come from ds_read_b64_tr_b16. Within each group
+//    of 16 lanes, lane i receives element (i % 4) of the 8 bytes addressed by lanes
+//    4k + i / 4, k = 0..3. When lane s of the group addresses key key0 + s / 4, channels
+//    base + 4 (s % 4) .. + 3, lane i therefore gets channel base + i of keys key0 .. key0 + 3:
+//    four keys of one channel, which is exactly a run of the PV MFMA's K dimension.
+// 16-byte chunks are XOR-swizzled per row (kv_swz) so that the 16 rows of a K read and the
+// 8 rows x 4 chunks of a V^T read both spread evenly over the LDS banks.
+
+typedef __attribute__((address_space(3))) char lchar;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per 256-byte row
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);              // 8 chunks per 128-byte row
+}
+
+template <int D, int BQ>
+struct DCfg {
+  static constexpr int NW = BQ / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWB = 2 * D;               // bytes per key row
+  static constexpr int TILE = BK * ROWB;           // bytes of one K (or V) block
+  static constexpr int INSTR = TILE / 1024;        // DMA instructions per tile
+  static constexpr int PER_WAVE = 2 * INSTR / NW;  // DMA instructions per wave per key block
+  static constexpr int OROW = D * 2 + 16;          // bytes per staged output row
+  static_assert((2 * INSTR) % NW == 0, "DMA instructions must split evenly over the waves");
+  static_assert(((NW + 1) / 2) * 32 * OROW <= 2 * TILE, "output staging must fit in one buffer");
+};
+
+// Issue this wave's share of the DMA copies of key block kb (K at buf, V at buf + TILE).
+// Keys past N are clamped to N - 1: their scores are masked, so the copy only has to be finite.
+template <int D, int BQ>
+__device__ __forceinline__ void dma_kv(const char* __restrict__ kbase, const char* __restrict__ vbase, int kb, int N,
+                                       lchar* buf) {
+  using C = DCfg<D, BQ>;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u) {
+    const int n = wave * C::PER_WAVE + u;
+    const bool isv = n >= C::INSTR;
+    const int m = isv ? n - C::INSTR : n;
+    const int byte = m * 1024 + lane * 16;
+    const int row = byte / C::ROWB;
+    const int chunk = ((byte % C::ROWB) >> 4) ^ kv_swz<D>(row);
+    const int key = min(kb * BK + row, N - 1);
+    const char* g = (isv ? vbase : kbase) + ((size_t)key * D + chunk * 8) * 2;
+    __builtin_amdgcn_global_load_lds(g, buf + (isv ? C::TILE : 0) + m * 1024, 16, 0, 0);
+  }
+}
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
+    void* __restrict__ o, float* __restrict__ lse) {
+  using C = DCfg<D, BQ>;
+  __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char buf1_[2 * C::TILE];
+  lchar* const buf0 = (lchar*)buf0_;
+  lchar* const buf1 = (lchar*)buf1_;
+
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / nqb;
+  const int qb = tile - bh * nqb;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31;
+  const int hf = lane >> 5;
+  const int cnt = min(max(kcnt[tile], 0), nkb);
+  const int32_t* list = kidx + (size_t)tile * nkb;
+
+  const size_t head_off = (size_t)bh * N * D * 2;
+  const char* qbase = static_cast<const char*>(q) + head_off;
+  const char* kbase = static_cast<const char*>(k) + head_off;
+  const char* vbase = static_cast<const char*>(v) + head_off;
+
+  if (cnt > 0) dma_kv<D, BQ>(kbase, vbase, list[0], N, buf0);
+
+  // Q^T fragments (B operand of S^T): query 32 wave + ln, channels 16 s + 8 hf .. + 7
+  const int qrow = qb * BQ + wave * 32 + ln;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const uint4 x = qrow < N ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * s + 8 * hf) * 2)
+                             : make_uint4(0, 0, 0, 0);
+    qf[s] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  // lane-constant LDS offsets of the K and V^T fragments
+  int koff[D / 16];
+  {
+    const int sw = kv_swz<D>(ln);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) koff[s] = ln * C::ROWB + (((2 * s + hf) ^ sw) << 4);
+  }
+  int voff[D / 32][2];
+  {
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int half = grp >> 1, gsub = grp & 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 8 * u + 4 * half + (i16 >> 2);
+      const int sw = kv_swz<D>(row);
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) {
+        const int chunk = 4 * r + 2 * gsub + ((i16 & 3) >> 1);
+        voff[r][u] = C::TILE + row * C::ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
+      }
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
+  float m_run = -INFINITY;  // running max in the scaled log2 domain, shared by the lane pair
+  float l_run = 0.f;        // this lane's part of the running sum
+  const bool ragged = (N % BK) != 0;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto iter = [&](lchar* cur, lchar* nxt, int t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block t is in `cur`; every wave is done with `nxt`
+    if (t + 1 < cnt) dma_kv<D, BQ>(kbase, vbase, list[t + 1], N, nxt);
+    const int kb = list[t];
+
+    f32x16 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.f;
+      s1[i] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(cur + koff[s]);
+      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(cur + koff[s] + 32 * C::ROWB);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+    }
+    if (ragged && kb == nkb - 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (key >= N) s0[i] = -INFINITY;
+        if (key + 32 >= N) s1[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = partner32_max(mx) * c_log2;
+    // Rescale only when some row's maximum grew by more than 2^8: until then exp2 values stay
+    // below 256, and O and l keep a common, slightly stale reference, which divides out exactly.
+    if (__ballot(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
+      m_run = m_new;
+    }
+    // P^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t; the row
+    // sum adds the same bf16 values the PV product uses.
+    bf16x8 pb[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
+        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
+      }
+      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    }
+    l_run += rs;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(cur + voff[r][0] + c * 16 * C::ROWB));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(cur + voff[r][1] + c * 16 * C::ROWB));
+        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
+      }
+  };
+
+  for (int t = 0; t < cnt; t += 2) {
+    iter(buf0, buf1, t);
+    if (t + 1 < cnt) iter(buf1, buf0, t + 1);
+  }
+  __syncthreads();
+
+  // epilogue: O = O^T / l, staged through LDS (two waves per buffer) for row-contiguous stores
+  const float l_tot = partner32_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  lchar* ol = ((wave & 1) ? buf1 : buf0) + (wave >> 1) * 32 * C::OROW;
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = 32 * r + 8 * a + 4 * hf;
+      const u32x2 w = {pack_bf16(oacc[r][4 * a] * inv, oacc[r][4 * a + 1] * inv),
+                       pack_bf16(oacc[r][4 * a + 2] * inv, oacc[r][4 * a + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(ol + ln * C::OROW + ch * 2) = w;
+    }
+  __syncthreads();
+  constexpr int CH16 = D * 2 / 16;
+  char* obase = static_cast<char*>(o) + head_off;
+#pragma unroll
+  for (int e = lane; e < 32 * CH16; e += 64) {
+    const int r = e / CH16, cc = e % CH16;
+    const int qr = qb * BQ + wave * 32 + r;
+    if (qr < N)
+      *reinterpret_cast<u32x4*>(obase + (size_t)qr * D * 2 + cc * 16) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ol + r * C::OROW + cc * 16);
+  }
+  if (lse != nullptr && hf == 0 && qrow < N) {
+    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream) {
@@ -320,8 +564,12 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
 template <int DT, int D, int BQ>
 static void launch_attn_t(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
                           int BH, int N, int nqb, int nkb, float c_log2, void* o, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, BQ>), dim3((unsigned)(BH * nqb)), dim3(AttnCfg<DT, D, BQ>::NT), 0, stream,
-                     q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
+  if constexpr (DT == kBF16)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
+                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
+  else
+    hipLaunchKernelGGL((attn_fwd_staged_kernel<DT, D, BQ>), dim3((unsigned)(BH * nqb)), dim3(AttnCfg<DT, D, BQ>::NT),
+                       0, stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
 }
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
