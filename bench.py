@@ -105,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="wan720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=240)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes --steps times (to calibrate "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count) and exit")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -116,6 +119,15 @@ def main(argv=None):
 
     import numpy as np
     import torch
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4,
+                          "launches": args.steps}))
+        return 0
     sys.path.insert(0, ROOT)
     import block_sparse_attention_query_amd as sa
     from workloads import WORKLOADS, make_inputs

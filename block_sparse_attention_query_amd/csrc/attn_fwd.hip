@@ -16,6 +16,8 @@
 // P^T never leaves registers: the MFMA result layout of S^T is reused as the B operand of the
 // PV product, and V^T is written to LDS with its keys permuted to match that layout.
 // K/V blocks are double-buffered through LDS with register staging, one barrier per block.
+#include <type_traits>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -350,25 +352,54 @@ struct DCfg {
   static_assert(((NW + 1) / 2) * 32 * OROW <= 2 * TILE, "output staging must fit in one buffer");
 };
 
-// Issue this wave's share of the DMA copies of key block kb (K at buf, V at buf + TILE).
-// Keys past N are clamped to N - 1: their scores are masked, so the copy only has to be finite.
+// Per-lane byte offsets, relative to the first row of a key block, of this wave's DMA copies:
+// instruction u of wave w copies 1 KiB stretch n = w * PER_WAVE + u of the K tile (n < INSTR) or
+// of the V tile; lane i fills bytes 16 i .. 16 i + 15 of it, i.e. row (n * 1024 + 16 i) / ROWB and
+// swizzled chunk slot ((n * 1024 + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
 template <int D, int BQ>
-__device__ __forceinline__ void dma_kv(const char* __restrict__ kbase, const char* __restrict__ vbase, int kb, int N,
-                                       lchar* buf) {
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[DCfg<D, BQ>::PER_WAVE],
+                                            int (&row)[DCfg<D, BQ>::PER_WAVE]) {
   using C = DCfg<D, BQ>;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
     const int n = wave * C::PER_WAVE + u;
-    const bool isv = n >= C::INSTR;
-    const int m = isv ? n - C::INSTR : n;
+    const int m = n >= C::INSTR ? n - C::INSTR : n;
     const int byte = m * 1024 + lane * 16;
-    const int row = byte / C::ROWB;
-    const int chunk = ((byte % C::ROWB) >> 4) ^ kv_swz<D>(row);
-    const int key = min(kb * BK + row, N - 1);
-    const char* g = (isv ? vbase : kbase) + ((size_t)key * D + chunk * 8) * 2;
-    __builtin_amdgcn_global_load_lds(g, buf + (isv ? C::TILE : 0) + m * 1024, 16, 0, 0);
+    row[u] = byte / C::ROWB;
+    const int chunk = ((byte % C::ROWB) >> 4) ^ kv_swz<D>(row[u]);
+    off[u] = (uint32_t)((row[u] * D + chunk * 8) * 2);
+  }
+}
+
+// Issue this wave's DMA copies of key block kb (K at buf, V at buf + TILE). In a ragged last
+// block, keys past N are clamped to N - 1: their scores are masked, so the copy only has to be
+// finite and in bounds.
+template <int D, int BQ>
+__device__ __forceinline__ void dma_kv(const char* __restrict__ kbase, const char* __restrict__ vbase, int kb,
+                                       int N, int wave, const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE],
+                                       const int (&row)[DCfg<D, BQ>::PER_WAVE], lchar* buf) {
+  using C = DCfg<D, BQ>;
+  const size_t blk = (size_t)kb * BK * C::ROWB;
+  if (kb * BK + BK <= N) {
+#pragma unroll
+    for (int u = 0; u < C::PER_WAVE; ++u) {
+      const int n = wave * C::PER_WAVE + u;
+      const bool isv = n >= C::INSTR;
+      const int m = isv ? n - C::INSTR : n;
+      __builtin_amdgcn_global_load_lds((isv ? vbase : kbase) + blk + off[u], buf + (isv ? C::TILE : 0) + m * 1024,
+                                       16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::PER_WAVE; ++u) {
+      const int n = wave * C::PER_WAVE + u;
+      const bool isv = n >= C::INSTR;
+      const int m = isv ? n - C::INSTR : n;
+      const int over = kb * BK + row[u] - (N - 1);
+      const uint32_t o = over > 0 ? off[u] - (uint32_t)(over * C::ROWB) : off[u];
+      __builtin_amdgcn_global_load_lds((isv ? vbase : kbase) + blk + o, buf + (isv ? C::TILE : 0) + m * 1024,
+                                       16, 0, 0);
+    }
   }
 }
 
@@ -386,7 +417,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: SGPR
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31;
   const int hf = lane >> 5;
@@ -398,7 +429,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const char* kbase = static_cast<const char*>(k) + head_off;
   const char* vbase = static_cast<const char*>(v) + head_off;
 
-  if (cnt > 0) dma_kv<D, BQ>(kbase, vbase, list[0], N, buf0);
+  uint32_t doff[C::PER_WAVE];
+  int drow[C::PER_WAVE];
+  dma_offsets<D, BQ>(wave, lane, doff, drow);
+  if (cnt > 0) dma_kv<D, BQ>(kbase, vbase, list[0], N, wave, doff, drow, buf0);
 
   // Q^T fragments (B operand of S^T): query 32 wave + ln, channels 16 s + 8 hf .. + 7
   const int qrow = qb * BQ + wave * 32 + ln;
@@ -443,10 +477,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const bool ragged = (N % BK) != 0;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto iter = [&](lchar* cur, lchar* nxt, int t) {
+  // One kept key block. RAGGED (compile time) masks keys past N; only the last list entry can
+  // be the ragged final key block because lists are ascending.
+  auto iter = [&](lchar* cur, lchar* nxt, int t, auto ragged_tag) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block t is in `cur`; every wave is done with `nxt`
-    if (t + 1 < cnt) dma_kv<D, BQ>(kbase, vbase, list[t + 1], N, nxt);
+    if (t + 1 < cnt) dma_kv<D, BQ>(kbase, vbase, list[t + 1], N, wave, doff, drow, nxt);
     const int kb = list[t];
 
     f32x16 s0, s1;
@@ -462,7 +499,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
     }
-    if (ragged && kb == nkb - 1) {
+    if (RAGGED) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -470,9 +507,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
         if (key + 32 >= N) s1[i] = -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    // row max as four independent v_max3_f32 chains (short dependency paths)
+    float m4[4];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    for (int c = 0; c < 4; ++c) m4[c] = fmaxf(s0[c], s1[c]);
+#pragma unroll
+    for (int i = 4; i < 16; ++i) m4[i & 3] = fmaxf(fmaxf(m4[i & 3], s0[i]), s1[i]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = partner32_max(mx) * c_log2;
     // Rescale only when some row's maximum grew by more than 2^8: until then exp2 values stay
     // below 256, and O and l keep a common, slightly stale reference, which divides out exactly.
@@ -489,7 +530,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     // P^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t; the row
     // sum adds the same bf16 values the PV product uses.
     bf16x8 pb[4];
-    float rs = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t w0[4], w1[4];
@@ -499,13 +540,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
                           __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
         w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
                           __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
+        rs[(e & 1) * 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs[(e & 1) * 2], false);
+        rs[(e & 1) * 2 + 1] =
+            __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs[(e & 1) * 2 + 1], false);
       }
       pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
       pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
     }
-    l_run += rs;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -519,9 +561,21 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       }
   };
 
-  for (int t = 0; t < cnt; t += 2) {
-    iter(buf0, buf1, t);
-    if (t + 1 < cnt) iter(buf1, buf0, t + 1);
+  using no_tail = std::integral_constant<bool, false>;
+  using tail = std::integral_constant<bool, true>;
+  const bool ragged_last = cnt > 0 && ragged && list[cnt - 1] == nkb - 1;
+  int t = 0;
+  for (; t + 2 < cnt; t += 2) {
+    iter(buf0, buf1, t, no_tail{});
+    iter(buf1, buf0, t + 1, no_tail{});
+  }
+  if (t + 1 < cnt) {
+    iter(buf0, buf1, t, no_tail{});
+    if (ragged_last) iter(buf1, buf0, t + 1, tail{});
+    else iter(buf1, buf0, t + 1, no_tail{});
+  } else if (t < cnt) {
+    if (ragged_last) iter(buf0, buf1, t, tail{});
+    else iter(buf0, buf1, t, no_tail{});
   }
   __syncthreads();
 

@@ -16,11 +16,13 @@ enum DType { kBF16 = 0, kF32 = 1 };
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two fp32 -> packed bf16 pair (round to nearest even; gfx950 v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 // Value of the same register in lane (lane ^ 32): v_permlane32_swap exchanges the upper half

@@ -13,8 +13,9 @@
 // except for rows that sit within rounding of a threshold.
 //
 // Kernel 1 (scores_kernel) is a small float64 GEMM per head written straight into `probs`.
-// Kernel 2 (select_kernel) takes one row per workgroup: softmax in place, a bitonic sort of
-// (P, index) pairs in LDS, a chunked prefix sum for m*, then the mask row and optional lists.
+// Kernel 2 (select_kernel) takes one row per workgroup: softmax in place, then orders only the
+// entries that can belong to the kept prefix, a chunked prefix sum for m*, then the mask row and
+// optional lists.
 #include "sa_common.h"
 
 namespace sa {
@@ -87,23 +88,44 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-// (key, index) a ranks before b: larger probability first, then the lower block index.
+// (P, index) a ranks before b: larger probability first, then the lower block index. P >= 0,
+// so comparing IEEE bit patterns as unsigned integers orders like the values.
 __device__ __forceinline__ bool ranks_before(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// Dynamic LDS layout for a row padded to `np2` entries (a power of two >= nkb):
-//   uint64 key[np2] | double red[8] | double scan[256] | uint16 idx[np2] | uint8 flag[np2]
+constexpr int NBUCKET = 128;    // half-octave buckets of P: bucket 2o + (lower half of octave o)
+constexpr int RANK_MAX = 2048;  // candidates ordered by rank counting up to this many; sorted above
+constexpr double FIX = 4503599627370496.0;  // 2^52: fixed-point scale of the bucket masses
+
+// Monotone non-increasing in P: a larger probability never lands in a later bucket.
+__device__ __forceinline__ int bucket_of(uint64_t bits) {
+  const int o = 1023 - (int)(bits >> 52);          // P in [2^-o, 2^(1-o)); P = 0 gives o = 1023
+  const int lower = (int)((~bits >> 51) & 1ull);   // mantissa top bit clear: lower half-octave
+  return min(NBUCKET - 1, 2 * max(o, 0) + lower);
+}
+
+// Dynamic LDS for a row of nkb entries (np2 = next power of two >= nkb):
+//   uint64 pk[np2] | uint64 hmass[128] | uint32 hcnt[128] | uint16 cand[np2] | uint16 ord[np2] |
+//   uint8 flag[np2]
+// Steps: softmax in place (pk holds S, then exp, then P bits); bucket histogram of P with integer
+// atomics (count and 2^-52 fixed-point mass, both order-independent); the first bucket prefix
+// whose count reaches k and whose mass reaches p + 1e-12 gives a candidate set that is closed
+// under ">=" and therefore holds the whole kept prefix; candidates are ordered exactly (rank
+// counting, or a bitonic sort when there are many); float64 running sums over that order give m*.
 __global__ __launch_bounds__(256) void select_kernel(double* __restrict__ probs, uint8_t* __restrict__ mask,
                                                      int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt,
                                                      int nkb, int np2, int k, double p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  uint64_t* key = reinterpret_cast<uint64_t*>(lds);
-  double* red = reinterpret_cast<double*>(key + np2);
-  double* scan = red + 8;
-  uint16_t* idx = reinterpret_cast<uint16_t*>(scan + 256);
-  uint8_t* flag = reinterpret_cast<uint8_t*>(idx + np2);
-  __shared__ int m_star_s;
+  uint64_t* pk = reinterpret_cast<uint64_t*>(lds);
+  uint64_t* hmass = pk + np2;
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(hmass + NBUCKET);
+  uint16_t* cand = reinterpret_cast<uint16_t*>(hcnt + NBUCKET);
+  uint16_t* ord = cand + np2;
+  uint8_t* flag = reinterpret_cast<uint8_t*>(ord + np2);
+  __shared__ double red[8];
+  __shared__ double scan[256];
+  __shared__ int n_cand, b_star, m_star_s;
   __shared__ int wcnt[4];
 
   const int tid = threadIdx.x;
@@ -114,62 +136,127 @@ __global__ __launch_bounds__(256) void select_kernel(double* __restrict__ probs,
 
   // softmax over the row (scores were written into `probs` by kernel 1)
   double mx = -INFINITY;
-  for (int j = tid; j < nkb; j += 256) mx = fmax(mx, P[j]);
+  for (int j = tid; j < nkb; j += 256) {
+    const double sj = P[j];
+    pk[j] = (uint64_t)__double_as_longlong(sj);
+    mx = fmax(mx, sj);
+  }
+  for (int j = tid; j < np2; j += 256) flag[j] = 0;
+  if (tid < NBUCKET) {
+    hcnt[tid] = 0;
+    hmass[tid] = 0;
+  }
+  if (tid == 0) {
+    n_cand = 0;
+    m_star_s = nkb;
+  }
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
   double sum = 0.0;
   for (int j = tid; j < nkb; j += 256) {
-    const double e = exp(P[j] - mx);
-    key[j] = __double_as_longlong(e);
+    const double e = exp(__longlong_as_double(pk[j]) - mx);
+    pk[j] = (uint64_t)__double_as_longlong(e);
     sum += e;
   }
   sum = wave_sum(sum);
   if (lane == 0) red[4 + wave] = sum;
-  if (tid == 0) m_star_s = nkb;
   __syncthreads();
   sum = ((red[4] + red[5]) + red[6]) + red[7];
-  for (int j = tid; j < np2; j += 256) {
-    if (j < nkb) {
-      const double pj = __longlong_as_double(key[j]) / sum;
-      P[j] = pj;
-      key[j] = (uint64_t)__double_as_longlong(pj);  // pj >= 0: the bit pattern orders like the value
-    } else {
-      key[j] = 0;  // padding sorts after every real entry (equal key, larger index)
-    }
-    idx[j] = (uint16_t)j;
-    flag[j] = 0;
+  for (int j = tid; j < nkb; j += 256) {
+    const double pj = __longlong_as_double(pk[j]) / sum;
+    P[j] = pj;
+    const uint64_t bits = (uint64_t)__double_as_longlong(pj);
+    pk[j] = bits;
+    const int b = bucket_of(bits);
+    atomicAdd(&hcnt[b], 1u);
+    atomicAdd(reinterpret_cast<unsigned long long*>(&hmass[b]), (unsigned long long)(pj * FIX));
   }
   __syncthreads();
 
-  // bitonic sort into ranks_before order
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (np2 >> 1); t += 256) {
-        const int lo = 2 * stride * (t / stride) + (t % stride);
-        const int hi = lo + stride;
-        const uint64_t ka = key[lo], kb = key[hi];
-        const uint32_t ia = idx[lo], ib = idx[hi];
-        const bool want_before = (lo & size) == 0;
-        if (ranks_before(kb, ib, ka, ia) == want_before) {
-          key[lo] = kb;
-          key[hi] = ka;
-          idx[lo] = (uint16_t)ib;
-          idx[hi] = (uint16_t)ia;
-        }
+  // first bucket prefix holding >= k entries and (for p > 0) mass >= p + 1e-12
+  if (wave == 0) {
+    const unsigned long long need = p > 0.0 ? (unsigned long long)ceil((p + 1e-12) * FIX) : 0ull;
+    unsigned c0 = hcnt[2 * lane], c1 = hcnt[2 * lane + 1];
+    unsigned long long m0 = hmass[2 * lane], m1 = hmass[2 * lane + 1];
+    unsigned cs = c0 + c1;
+    unsigned long long ms = m0 + m1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {  // inclusive scan over lanes
+      const unsigned cu = __shfl_up(cs, o, 64);
+      const unsigned long long mu = __shfl_up(ms, o, 64);
+      if (lane >= o) {
+        cs += cu;
+        ms += mu;
       }
-      __syncthreads();
     }
+    const unsigned cb = cs - c0 - c1;  // exclusive prefix before bucket 2 lane
+    const unsigned long long mb = ms - m0 - m1;
+    const bool ok0 = cb + c0 >= (unsigned)k && mb + m0 >= need;
+    const bool ok1 = cs >= (unsigned)k && ms >= need;
+    const uint64_t b0 = __ballot(ok0), b1 = __ballot(ok1);
+    int bs = NBUCKET - 1;
+    if (b0 | b1) {
+      const int l0 = b0 ? __ffsll((unsigned long long)b0) - 1 : 64;
+      const int l1 = b1 ? __ffsll((unsigned long long)b1) - 1 : 64;
+      bs = min(2 * l0, 2 * l1 + 1);
+    }
+    if (lane == 0) b_star = bs;
   }
+  __syncthreads();
+  const int bs = b_star;
+  for (int j = tid; j < nkb; j += 256) {
+    if (bucket_of(pk[j]) <= bs) cand[atomicAdd(&n_cand, 1)] = (uint16_t)j;
+  }
+  __syncthreads();
+  const int S = n_cand;
 
-  // Top-p: m* = min{m >= 1 : P_(1) + ... + P_(m) >= p}, or nkb if the sum never reaches p.
+  // exact order of the candidates
+  if (S <= RANK_MAX) {
+    for (int c = tid; c < S; c += 256) {
+      const uint32_t jc = cand[c];
+      const uint64_t kc = pk[jc];
+      int rank = 0;
+      for (int x = 0; x < S; ++x) {
+        const uint32_t jx = cand[x];
+        rank += ranks_before(pk[jx], jx, kc, jc) ? 1 : 0;
+      }
+      ord[rank] = (uint16_t)jc;
+    }
+  } else {
+    int sp2 = 1;
+    while (sp2 < S) sp2 <<= 1;
+    for (int c = S + tid; c < sp2; c += 256) cand[c] = 0xffff;  // padding ranks last
+    __syncthreads();
+    for (int size = 2; size <= sp2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < (sp2 >> 1); t += 256) {
+          const int lo = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+          const int hi = lo + stride;
+          const uint32_t ja = cand[lo], jb = cand[hi];
+          const uint64_t ka = ja == 0xffff ? 0 : pk[ja], kb = jb == 0xffff ? 0 : pk[jb];
+          const bool b_first = (jb != 0xffff) && (ja == 0xffff || ranks_before(kb, jb, ka, ja));
+          if (b_first == ((lo & size) == 0)) {
+            cand[lo] = (uint16_t)jb;
+            cand[hi] = (uint16_t)ja;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int c = tid; c < S; c += 256) ord[c] = cand[c];
+  }
+  __syncthreads();
+
+  // Top-p: m* = min{m >= 1 : P_(1) + ... + P_(m) >= p}, or nkb if the sum never reaches p. The
+  // candidates hold every prefix that can reach p (or all entries when the row's mass is short).
   int m_star = 0;
   if (p > 0.0) {
-    const int per = (nkb + 255) / 256;
-    const int lo = tid * per, hi = min(nkb, lo + per);
+    const int per = (S + 255) / 256;
+    const int lo = tid * per, hi = min(S, lo + per);
     double local = 0.0;
-    for (int r = lo; r < hi; ++r) local += __longlong_as_double(key[r]);
+    for (int r = lo; r < hi; ++r) local += __longlong_as_double(pk[ord[r]]);
     scan[tid] = local;
     __syncthreads();
     if (wave == 0) {  // exclusive scan of the 256 chunk sums, in order
@@ -194,7 +281,7 @@ __global__ __launch_bounds__(256) void select_kernel(double* __restrict__ probs,
     __syncthreads();
     double c = scan[tid];
     for (int r = lo; r < hi; ++r) {
-      c += __longlong_as_double(key[r]);
+      c += __longlong_as_double(pk[ord[r]]);
       if (c >= p) {
         atomicMin(&m_star_s, r + 1);
         break;
@@ -203,9 +290,9 @@ __global__ __launch_bounds__(256) void select_kernel(double* __restrict__ probs,
     __syncthreads();
     m_star = m_star_s;
   }
-  const int L = max(k, m_star);
+  const int L = min(max(k, m_star), S);
 
-  for (int r = tid; r < L; r += 256) flag[idx[r]] = 1;
+  for (int r = tid; r < L; r += 256) flag[ord[r]] = 1;
   __syncthreads();
   uint8_t* mrow = mask + row * (size_t)nkb;
   for (int j = tid; j < nkb; j += 256) mrow[j] = flag[j];
@@ -237,7 +324,7 @@ int select_np2(int nkb) {
 }
 
 size_t select_lds_bytes(int np2) {
-  return (size_t)np2 * 8 + 8 * 8 + 256 * 8 + (size_t)np2 * 2 + (size_t)np2;
+  return (size_t)np2 * 8 + NBUCKET * 8 + NBUCKET * 4 + (size_t)np2 * 2 * 2 + (size_t)np2;
 }
 
 hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, int nkb, int d, double scale,
