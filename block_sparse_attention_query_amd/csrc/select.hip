@@ -12,7 +12,7 @@
 // Everything that decides the mask is float64 so that it agrees with a float64 reference
 // except for rows that sit within rounding of a threshold.
 //
-// Kernel 1 (scores_kernel) is a small float64 GEMM per head written straight into `probs`.
+// Kernel 1 (scores_kernel) is a float64 GEMM per head on the matrix cores, written into `probs`.
 // Kernel 2 (select_kernel) takes one row per workgroup: softmax in place, then orders only the
 // entries that can belong to the kept prefix, a chunked prefix sum for m*, then the mask row and
 // optional lists.
@@ -22,55 +22,66 @@ namespace sa {
 
 // ---------------------------------------------------------------- kernel 1: pooled scores
 
-constexpr int ST = 64;   // output tile edge
-constexpr int SKD = 16;  // depth of one LDS stage
+// S = scale * Qbar Kbar^T per head in float64 on the matrix cores (v_mfma_f64_16x16x4f64). For
+// that instruction lane j holds A[j % 16][j / 16] and B[j / 16][j % 16] of a 16x4 / 4x16 step, and
+// element i of the result holds C[4 i + j / 16][j % 16] (lane layout checked with one-hot
+// operands). A workgroup of 4 waves computes a 64 x 64 tile: the 64 key-block rows of Kbar sit in
+// LDS (two doubles of padding per row put the 32 lanes of each half-wave read -- 16 rows x 2
+// consecutive doubles -- on distinct banks), and wave w
+// keeps its 16 query-block rows of Qbar in registers.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int ST = 64;  // output tile edge
 
+template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
-                                                     int nqb, int nkb, int d, double scale,
-                                                     double* __restrict__ s_out) {
-  __shared__ double As[SKD][ST + 1];
-  __shared__ double Bs[SKD][ST + 1];
+                                                     int nqb, int nkb, double scale, double* __restrict__ s_out) {
+  constexpr int LROW = D + 2;
+  __shared__ double kl[ST * LROW];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * ST;
   const int j0 = blockIdx.x * ST;
-  const double* qh = qp + (size_t)bh * nqb * d;
-  const double* kh = kp + (size_t)bh * nkb * d;
-  const int tj = threadIdx.x & 15;  // columns j0 + tj + 16 b
-  const int ti = threadIdx.x >> 4;  // rows    i0 + ti + 16 a
-  double acc[4][4] = {};
-  for (int d0 = 0; d0 < d; d0 += SKD) {
+  const double* qh = qp + (size_t)bh * nqb * D;
+  const double* kh = kp + (size_t)bh * nkb * D;
+  const int tid = threadIdx.x;
+  {
+    // all of this thread's loads first, then the LDS stores (no load waits inside a loop)
+    constexpr int PER = ST * D / 256;
+    double v[PER];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = threadIdx.x + 256 * e;
-      const int r = idx >> 4, c = idx & 15;
-      As[c][r] = (i0 + r < nqb) ? qh[(size_t)(i0 + r) * d + d0 + c] : 0.0;
-      Bs[c][r] = (j0 + r < nkb) ? kh[(size_t)(j0 + r) * d + d0 + c] : 0.0;
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / D, c = e % D;
+      v[u] = (j0 + r < nkb) ? kh[(size_t)(j0 + r) * D + c] : 0.0;
     }
-    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < SKD; ++c) {
-      double a[4], b[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        a[x] = As[c][ti + 16 * x];
-        b[x] = Bs[c][tj + 16 * x];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      kl[(e / D) * LROW + e % D] = v[u];
     }
-    __syncthreads();
   }
+  const int wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, kq = lane >> 4;
+  const int qrow = i0 + 16 * wave + m;
+  double a[D / 4];
+#pragma unroll
+  for (int s = 0; s < D / 4; ++s) a[s] = qrow < nqb ? qh[(size_t)qrow * D + 4 * s + kq] : 0.0;
+  __syncthreads();
+  f64x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = (f64x4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < D / 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], kl[(16 * t + m) * LROW + 4 * s + kq], acc[t], 0, 0, 0);
   double* so = s_out + (size_t)bh * nqb * nkb;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = i0 + ti + 16 * x;
-    if (i >= nqb) continue;
+  for (int t = 0; t < 4; ++t) {
+    const int col = j0 + 16 * t + m;
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int j = j0 + tj + 16 * y;
-      if (j < nkb) so[(size_t)i * nkb + j] = scale * acc[x][y];
+    for (int i = 0; i < 4; ++i) {
+      const int row = i0 + 16 * wave + 4 * i + kq;
+      if (row < nqb && col < nkb) so[(size_t)row * nkb + col] = scale * acc[t][i];
     }
   }
 }
@@ -317,6 +328,252 @@ __global__ __launch_bounds__(256) void select_kernel(double* __restrict__ probs,
   }
 }
 
+// ---------------------------------------------------------------- kernel 2b: one wave per row
+
+// Rows of up to WAVE_NKB entries take one wave each (four rows per workgroup, no workgroup
+// barrier). Entry j of the row stays in lane j % 64, register slot j / 64, for the whole
+// selection. Wave sums and maxima combine within each 16-lane row with DPP moves and then add the
+// four row results, read from lanes 0, 16, 32 and 48, in a fixed order: every lane gets the same
+// value, identical from run to run.
+//
+// Selection without sorting the row. Let key(P) be the IEEE bits of P (ordered like P, as P >= 0)
+// and f(T) the predicate "at least k entries have key >= T and, for p > 0, their mass is >= p".
+// f is monotone; with T* = max{T : f(T)} the kept prefix holds every entry whose key is above T*,
+// none below it, and a leading run, in index order, of the entries whose key equals T* (the
+// prefix through T* meets both thresholds; the part above T* misses one of them). T* is
+// bracketed by bisection, first over the 128 half-octave bucket edges, then over key values while
+// more than 64 entries lie inside the bracket [lo, hi]. The entries inside are put in exact order,
+// by rank counting (at most 64 of them, one per lane) or, when the bracket has closed on a single
+// value, by index, and running sums along that order give m*.
+constexpr int WAVE_NKB = 2048;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1, lane ^ 2), row_ror:4, row_ror:8.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_dpp(double x) {
+  x += dpp_f64<DPP_XOR1>(x);
+  x += dpp_f64<DPP_XOR2>(x);
+  x += dpp_f64<DPP_ROR4>(x);
+  x += dpp_f64<DPP_ROR8>(x);
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+__device__ __forceinline__ double wave_max_dpp(double x) {
+  x = fmax(x, dpp_f64<DPP_XOR1>(x));
+  x = fmax(x, dpp_f64<DPP_XOR2>(x));
+  x = fmax(x, dpp_f64<DPP_ROR4>(x));
+  x = fmax(x, dpp_f64<DPP_ROR8>(x));
+  return fmax(fmax(readlane_f64(x, 0), readlane_f64(x, 16)), fmax(readlane_f64(x, 32), readlane_f64(x, 48)));
+}
+
+// Smallest key of bucket b (bucket_of(key) <= b exactly when key >= bucket_floor(b)).
+__device__ __forceinline__ int64_t bucket_floor(int b) {
+  if (b >= NBUCKET - 1) return 0;
+  const int64_t e = 1023 - (b >> 1);
+  return (e << 52) | ((b & 1) ? (int64_t)0 : ((int64_t)1 << 51));
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ probs, uint8_t* __restrict__ mask,
+                                                          int32_t* __restrict__ kept_idx,
+                                                          int32_t* __restrict__ kept_cnt, int rows, int nkb, int k,
+                                                          double p) {
+  __shared__ int64_t s_key[4][64];
+  __shared__ double s_val[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  if (row >= (size_t)rows) return;  // whole wave leaves; nothing below synchronises the workgroup
+  const uint64_t below = (1ull << lane) - 1ull;
+  double* P = probs + row * (size_t)nkb;
+
+  // softmax of the row (kernel 1 left the scores in `probs`); P is written back in place
+  int64_t key[R];  // key of entry 64 u + lane, -1 past the end of the row
+  {
+    double v[R];
+    double mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int j = 64 * u + lane;
+      v[u] = j < nkb ? P[j] : -INFINITY;
+      mx = fmax(mx, v[u]);
+    }
+    mx = wave_max_dpp(mx);
+    double sum = 0.0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (64 * u + lane < nkb) {
+        v[u] = exp(v[u] - mx);
+        sum += v[u];
+      }
+    }
+    sum = wave_sum_dpp(sum);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int j = 64 * u + lane;
+      key[u] = -1;
+      if (j < nkb) {
+        const double pj = v[u] / sum;
+        P[j] = pj;
+        key[u] = __double_as_longlong(pj);
+      }
+    }
+  }
+
+  // count and mass of the entries with key >= T (count and mass are wave-uniform)
+  auto tally = [&](int64_t T, int& cnt, double& mass) {
+    int c = 0;
+    double m = 0.0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const bool ge = key[u] >= T;
+      c += __popcll(__ballot(ge));
+      m += ge ? __longlong_as_double(key[u]) : 0.0;
+    }
+    cnt = c;
+    mass = wave_sum_dpp(m);
+  };
+  auto meets = [&](int cnt, double mass) { return cnt >= k && (p <= 0.0 || mass >= p); };
+
+  int c_lo, c_hi;      // entries with key >= lo, and with key > hi
+  double m_lo, m_hi;   // their masses
+  tally(0, c_lo, m_lo);
+  const bool keep_all = !meets(c_lo, m_lo);  // the row's mass never reaches p: m* = nkb
+  int64_t lo = 0, hi = INT64_MAX;
+  int n_keep = 0;      // leading entries of the bracket, in selection order, that are kept
+  uint64_t kmask = 0;  // bracket positions kept when the bracket holds <= 64 entries
+  int nb = 0;
+  if (!keep_all) {
+    c_hi = 0;
+    m_hi = 0.0;
+    int blo = 0, bhi = NBUCKET - 1;  // f(bucket_floor(bhi)) holds, f(bucket_floor(blo - 1)) fails
+    while (blo < bhi) {
+      const int mid = (blo + bhi) >> 1;
+      int c;
+      double m;
+      tally(bucket_floor(mid), c, m);
+      if (meets(c, m)) {
+        bhi = mid;
+        c_lo = c;
+        m_lo = m;
+      } else {
+        blo = mid + 1;
+        c_hi = c;
+        m_hi = m;
+      }
+    }
+    lo = bucket_floor(blo);
+    hi = blo == 0 ? INT64_MAX : bucket_floor(blo - 1) - 1;
+    while (c_lo - c_hi > 64 && lo < hi) {
+      const int64_t mid = lo + ((hi - lo + 1) >> 1);
+      int c;
+      double m;
+      tally(mid, c, m);
+      if (meets(c, m)) {
+        lo = mid;
+        c_lo = c;
+        m_lo = m;
+      } else {
+        hi = mid - 1;
+        c_hi = c;
+        m_hi = m;
+      }
+    }
+    nb = c_lo - c_hi;
+    const int need_k = max(k - c_hi, 0);
+    if (nb <= 64) {
+      // gather the bracket (ascending index) one entry per lane, rank it, then running sums
+      int base = 0;
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const bool in = key[u] >= lo && key[u] <= hi;
+        const uint64_t bal = __ballot(in);
+        if (in) s_key[wave][base + __popcll(bal & below)] = key[u];
+        base += __popcll(bal);
+      }
+      wave_sync();
+      const bool mine = lane < nb;
+      const int64_t kc = mine ? s_key[wave][lane] : -1;
+      int rank = 0;
+      for (int x = 0; x < nb; ++x) {
+        const uint32_t xl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)kc, x);
+        const uint32_t xh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)kc >> 32), x);
+        const int64_t kx = (int64_t)(((uint64_t)xh << 32) | xl);
+        rank += (kx > kc || (kx == kc && x < lane)) ? 1 : 0;
+      }
+      int n_p = 0;
+      if (p > 0.0 && m_hi < p) {
+        if (mine) s_val[wave][rank] = __longlong_as_double(kc);
+        wave_sync();
+        double run = mine ? s_val[wave][lane] : 0.0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const double up = __shfl_up(run, o, 64);
+          if (lane >= o) run += up;
+        }
+        const uint64_t hit = __ballot(mine && m_hi + run >= p);
+        n_p = hit ? __ffsll((unsigned long long)hit) : nb;
+      }
+      n_keep = min(nb, max(need_k, n_p));
+      kmask = __ballot(mine && rank < n_keep);
+    } else {
+      // lo == hi: every entry in the bracket has the value v, and the order among them is by index
+      const double v = __longlong_as_double(lo);
+      int n_p = 0;
+      if (p > 0.0 && m_hi < p) n_p = v > 0.0 ? (int)min((double)nb, ceil((p - m_hi) / v)) : nb;
+      n_keep = min(nb, max(need_k, n_p));
+    }
+  }
+
+  uint8_t* mrow = mask + row * (size_t)nkb;
+  int32_t* out = kept_idx != nullptr ? kept_idx + row * (size_t)nkb : nullptr;
+  int pos0 = 0, n_out = 0;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int j = 64 * u + lane;
+    const bool in = key[u] >= lo && key[u] <= hi;
+    const uint64_t bal = __ballot(in);
+    const int pos = pos0 + __popcll(bal & below);
+    pos0 += __popcll(bal);
+    bool kept;
+    if (keep_all) kept = j < nkb;
+    else kept = key[u] > hi || (in && (nb <= 64 ? (pos < 64 && ((kmask >> pos) & 1ull) != 0) : pos < n_keep));
+    if (j < nkb) mrow[j] = kept ? 1 : 0;
+    if (out != nullptr) {
+      const uint64_t kb = __ballot(kept);
+      if (kept) out[n_out + __popcll(kb & below)] = j;
+      n_out += __popcll(kb);
+    }
+  }
+  if (out != nullptr && lane == 0) kept_cnt[row] = n_out;
+}
+
+template <int R>
+hipError_t launch_rows(double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, int rows, int nkb, int k,
+                       double p, hipStream_t stream) {
+  hipLaunchKernelGGL((select_rows_kernel<R>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, probs, mask,
+                     kept_idx, kept_cnt, rows, nkb, k, p);
+  return hipGetLastError();
+}
+
 int select_np2(int nkb) {
   int n = 1;
   while (n < nkb) n <<= 1;
@@ -331,9 +588,26 @@ hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, in
                          int k, double p, double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt,
                          hipStream_t stream) {
   const dim3 g1((unsigned)((nkb + ST - 1) / ST), (unsigned)((nqb + ST - 1) / ST), (unsigned)BH);
-  hipLaunchKernelGGL(scores_kernel, g1, dim3(256), 0, stream, qp, kp, nqb, nkb, d, scale, probs);
+  if (d == 128)
+    hipLaunchKernelGGL((scores_kernel<128>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, scale, probs);
+  else
+    hipLaunchKernelGGL((scores_kernel<64>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, scale, probs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nkb <= WAVE_NKB) {
+    const int rows = BH * nqb;
+    const int r = (nkb + 63) / 64;  // register slots per lane
+    if (r <= 1) return launch_rows<1>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 2) return launch_rows<2>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 4) return launch_rows<4>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 8) return launch_rows<8>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 12) return launch_rows<12>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 16) return launch_rows<16>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 20) return launch_rows<20>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 24) return launch_rows<24>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    if (r <= 28) return launch_rows<28>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+    return launch_rows<32>(probs, mask, kept_idx, kept_cnt, rows, nkb, k, p, stream);
+  }
   const int np2 = select_np2(nkb);
   const size_t lds = select_lds_bytes(np2);
   if (lds > 65536) {
