@@ -14,8 +14,11 @@
 //   max and row sum need one exchange with lane^32 (v_permlane32_swap)
 //   O^T (D x 32) += V^T_blk (LDS) x P^T (registers)             : (D/32) x 4 MFMA 32x32x16
 // P^T never leaves registers: the MFMA result layout of S^T is reused as the B operand of the
-// PV product, and V^T is written to LDS with its keys permuted to match that layout.
-// K/V blocks are double-buffered through LDS with register staging, one barrier per block.
+// PV product, so the V^T operand is read with its keys in that same order.
+// Two kernels share this scheme. The bf16 kernel copies K/V blocks HBM -> LDS with DMA loads and
+// reads V^T with transpose reads, in a two-stage software pipeline (scores of the next block
+// overlap the softmax and P V of the current one). The fp32 kernel stages blocks through
+// registers, rounding them to bf16, and writes V^T to LDS with its keys permuted.
 #include <type_traits>
 
 #include "sa_common.h"
@@ -198,14 +201,14 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_staged_kernel(
 
   uint4 st[C::TPT][8];
   if (cnt > 0) {
-    stage_load<DT, D, BQ>(kbase, vbase, list[0], N, st);
+    stage_load<DT, D, BQ>(kbase, vbase, min(max(list[0], 0), nkb - 1), N, st);
     stage_store<DT, D, BQ>(smem, st);
   }
   __syncthreads();
 
   for (int t = 0; t < cnt; ++t) {
-    const int kb = list[t];
-    if (t + 1 < cnt) stage_load<DT, D, BQ>(kbase, vbase, list[t + 1], N, st);
+    const int kb = min(max(list[t], 0), nkb - 1);  // clamped: no load leaves K or V
+    if (t + 1 < cnt) stage_load<DT, D, BQ>(kbase, vbase, min(max(list[t + 1], 0), nkb - 1), N, st);
     const char* kl = smem + (t & 1) * C::BUF;
     const char* vl = kl + C::KBYTES;
 
@@ -339,6 +342,7 @@ __device__ __forceinline__ int kv_swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);              // 8 chunks per 128-byte row
 }
 
+// Launch geometry: one workgroup per (b, h, query block), BQ / 32 waves.
 template <int D, int BQ>
 struct DCfg {
   static constexpr int NW = BQ / 32;
@@ -346,73 +350,71 @@ struct DCfg {
   static constexpr int ROWB = 2 * D;               // bytes per key row
   static constexpr int TILE = BK * ROWB;           // bytes of one K (or V) block
   static constexpr int INSTR = TILE / 1024;        // DMA instructions per tile
-  static constexpr int PER_WAVE = 2 * INSTR / NW;  // DMA instructions per wave per key block
+  static constexpr int PER_WAVE = INSTR / NW;      // DMA instructions per wave per tile
   static constexpr int OROW = D * 2 + 16;          // bytes per staged output row
-  static_assert((2 * INSTR) % NW == 0, "DMA instructions must split evenly over the waves");
-  static_assert(((NW + 1) / 2) * 32 * OROW <= 2 * TILE, "output staging must fit in one buffer");
+  static_assert(INSTR % NW == 0, "DMA instructions must split evenly over the waves");
+  static_assert(((NW + 1) / 2) * 32 * OROW <= 2 * TILE, "output staging must fit in one buffer pair");
 };
 
-// Per-lane byte offsets, relative to the first row of a key block, of this wave's DMA copies:
-// instruction u of wave w copies 1 KiB stretch n = w * PER_WAVE + u of the K tile (n < INSTR) or
-// of the V tile; lane i fills bytes 16 i .. 16 i + 15 of it, i.e. row (n * 1024 + 16 i) / ROWB and
-// swizzled chunk slot ((n * 1024 + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
+// Per-lane byte offsets, relative to the first row of a key block, of this wave's DMA copies of
+// one tile (K and V tiles share them): instruction u of wave w copies 1 KiB stretch
+// m = w * PER_WAVE + u; lane i fills bytes 16 i .. 16 i + 15 of it, i.e. row (m * 1024 + 16 i) / ROWB
+// and swizzled chunk slot ((m * 1024 + 16 i) % ROWB) / 16, which holds logical chunk
+// slot ^ kv_swz(row).
 template <int D, int BQ>
-__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[DCfg<D, BQ>::PER_WAVE],
-                                            int (&row)[DCfg<D, BQ>::PER_WAVE]) {
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[DCfg<D, BQ>::PER_WAVE]) {
   using C = DCfg<D, BQ>;
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
-    const int n = wave * C::PER_WAVE + u;
-    const int m = n >= C::INSTR ? n - C::INSTR : n;
-    const int byte = m * 1024 + lane * 16;
-    row[u] = byte / C::ROWB;
-    const int chunk = ((byte % C::ROWB) >> 4) ^ kv_swz<D>(row[u]);
-    off[u] = (uint32_t)((row[u] * D + chunk * 8) * 2);
+    const int byte = (wave * C::PER_WAVE + u) * 1024 + lane * 16;
+    const int row = byte / C::ROWB;
+    const int chunk = ((byte % C::ROWB) >> 4) ^ kv_swz<D>(row);
+    off[u] = (uint32_t)((row * D + chunk * 8) * 2);
   }
 }
 
-// Issue this wave's DMA copies of key block kb (K at buf, V at buf + TILE). In a ragged last
+// Issue this wave's DMA copies of the K or V tile of key block kb into dst. In a ragged last
 // block, keys past N are clamped to N - 1: their scores are masked, so the copy only has to be
 // finite and in bounds.
 template <int D, int BQ>
-__device__ __forceinline__ void dma_kv(const char* __restrict__ kbase, const char* __restrict__ vbase, int kb,
-                                       int N, int wave, const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE],
-                                       const int (&row)[DCfg<D, BQ>::PER_WAVE], lchar* buf) {
+__device__ __forceinline__ void dma_tile(const char* __restrict__ base, int kb, int N, int wave, int lane,
+                                         const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE], lchar* dst) {
   using C = DCfg<D, BQ>;
-  const size_t blk = (size_t)kb * BK * C::ROWB;
+  const char* blk = base + (size_t)kb * BK * C::ROWB;
   if (kb * BK + BK <= N) {
 #pragma unroll
-    for (int u = 0; u < C::PER_WAVE; ++u) {
-      const int n = wave * C::PER_WAVE + u;
-      const bool isv = n >= C::INSTR;
-      const int m = isv ? n - C::INSTR : n;
-      __builtin_amdgcn_global_load_lds((isv ? vbase : kbase) + blk + off[u], buf + (isv ? C::TILE : 0) + m * 1024,
-                                       16, 0, 0);
-    }
+    for (int u = 0; u < C::PER_WAVE; ++u)
+      __builtin_amdgcn_global_load_lds(blk + off[u], dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
   } else {
 #pragma unroll
     for (int u = 0; u < C::PER_WAVE; ++u) {
-      const int n = wave * C::PER_WAVE + u;
-      const bool isv = n >= C::INSTR;
-      const int m = isv ? n - C::INSTR : n;
-      const int over = kb * BK + row[u] - (N - 1);
+      const int row = ((wave * C::PER_WAVE + u) * 1024 + lane * 16) / C::ROWB;
+      const int over = kb * BK + row - (N - 1);
       const uint32_t o = over > 0 ? off[u] - (uint32_t)(over * C::ROWB) : off[u];
-      __builtin_amdgcn_global_load_lds((isv ? vbase : kbase) + blk + o, buf + (isv ? C::TILE : 0) + m * 1024,
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
     }
   }
 }
 
+// Main loop as a two-stage software pipeline over the kept list. Step t computes the scores of
+// block t + 1 on the matrix cores while the vector units turn the scores of block t into P and
+// the matrix cores then add P V of block t: the three are independent, so they share one basic
+// block and the compiler interleaves them. K therefore runs one block ahead of V in LDS: at step
+// t, K(t+1) and V(t) are resident and the DMA fills K(t+2) and V(t+1) into the buffers that
+// K(t) and V(t-1) left. The running maximum is raised after P V of block t, from the scores of
+// block t + 1, so the rare rescale branch closes the step instead of splitting it.
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
     void* __restrict__ o, float* __restrict__ lse) {
   using C = DCfg<D, BQ>;
-  __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];
-  __shared__ __attribute__((aligned(1024))) char buf1_[2 * C::TILE];
-  lchar* const buf0 = (lchar*)buf0_;
-  lchar* const buf1 = (lchar*)buf1_;
+  __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
+  lchar* const kb0 = (lchar*)kbuf_;
+  lchar* const kb1 = kb0 + C::TILE;
+  lchar* const vb0 = (lchar*)vbuf_;
+  lchar* const vb1 = vb0 + C::TILE;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
@@ -423,6 +425,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const int hf = lane >> 5;
   const int cnt = min(max(kcnt[tile], 0), nkb);
   const int32_t* list = kidx + (size_t)tile * nkb;
+  // list entries are clamped to [0, nKB) so that no load leaves K or V
+  auto blk = [&](int i) { return min(max(list[i], 0), nkb - 1); };
 
   const size_t head_off = (size_t)bh * N * D * 2;
   const char* qbase = static_cast<const char*>(q) + head_off;
@@ -430,21 +434,25 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const char* vbase = static_cast<const char*>(v) + head_off;
 
   uint32_t doff[C::PER_WAVE];
-  int drow[C::PER_WAVE];
-  dma_offsets<D, BQ>(wave, lane, doff, drow);
-  if (cnt > 0) dma_kv<D, BQ>(kbase, vbase, list[0], N, wave, doff, drow, buf0);
+  dma_offsets<D, BQ>(wave, lane, doff);
+  if (cnt > 0) {
+    dma_tile<D, BQ>(kbase, blk(0), N, wave, lane, doff, kb0);
+    dma_tile<D, BQ>(vbase, blk(0), N, wave, lane, doff, vb0);
+  }
+  if (cnt > 1) dma_tile<D, BQ>(kbase, blk(1), N, wave, lane, doff, kb1);
 
   // Q^T fragments (B operand of S^T): query 32 wave + ln, channels 16 s + 8 hf .. + 7
   const int qrow = qb * BQ + wave * 32 + ln;
+  const bool qvalid = qrow < N;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const uint4 x = qrow < N ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * s + 8 * hf) * 2)
-                             : make_uint4(0, 0, 0, 0);
+    const uint4 x = qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * s + 8 * hf) * 2)
+                           : make_uint4(0, 0, 0, 0);
     qf[s] = __builtin_bit_cast(bf16x8, x);
   }
 
-  // lane-constant LDS offsets of the K and V^T fragments
+  // lane-constant LDS offsets of the K and V^T fragments within a tile
   int koff[D / 16];
   {
     const int sw = kv_swz<D>(ln);
@@ -462,7 +470,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < D / 32; ++r) {
         const int chunk = 4 * r + 2 * gsub + ((i16 & 3) >> 1);
-        voff[r][u] = C::TILE + row * C::ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
+        voff[r][u] = row * C::ROWB + ((chunk ^ sw) << 4) + (i16 & 1) * 8;
       }
     }
   }
@@ -474,49 +482,45 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
   float m_run = -INFINITY;  // running max in the scaled log2 domain, shared by the lane pair
   float l_run = 0.f;        // this lane's part of the running sum
-  const bool ragged = (N % BK) != 0;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One kept key block. RAGGED (compile time) masks keys past N; only the last list entry can
-  // be the ragged final key block because lists are ascending.
-  auto iter = [&](lchar* cur, lchar* nxt, int t, auto ragged_tag) {
-    constexpr bool RAGGED = decltype(ragged_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block t is in `cur`; every wave is done with `nxt`
-    if (t + 1 < cnt) dma_kv<D, BQ>(kbase, vbase, list[t + 1], N, wave, doff, drow, nxt);
-    const int kb = list[t];
-
-    f32x16 s0, s1;
+  // S^T of the key block in kt (64 keys x 32 queries as two 32 x 32 tiles)
+  auto scores = [&](const lchar* kt, f32x16 (&sc)[2]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
+      sc[0][i] = 0.f;
+      sc[1][i] = 0.f;
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(cur + koff[s]);
-      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(cur + koff[s] + 32 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s]);
+      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s] + 32 * C::ROWB);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sc[1], 0, 0, 0);
     }
-    if (RAGGED) {
+  };
+  // keys past N (only in the ragged last key block kb) get score -inf
+  auto mask_tail = [&](f32x16 (&sc)[2], int kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (key >= N) s0[i] = -INFINITY;
-        if (key + 32 >= N) s1[i] = -INFINITY;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (key >= N) sc[0][i] = -INFINITY;
+      if (key + 32 >= N) sc[1][i] = -INFINITY;
     }
-    // row max as four independent v_max3_f32 chains (short dependency paths)
+  };
+  // maximum over the block's 64 keys of each query, scaled to the log2 domain
+  auto block_max = [&](const f32x16 (&sc)[2]) {
     float m4[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) m4[c] = fmaxf(s0[c], s1[c]);
+    for (int c = 0; c < 4; ++c) m4[c] = fmaxf(sc[0][c], sc[1][c]);
 #pragma unroll
-    for (int i = 4; i < 16; ++i) m4[i & 3] = fmaxf(fmaxf(m4[i & 3], s0[i]), s1[i]);
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = partner32_max(mx) * c_log2;
-    // Rescale only when some row's maximum grew by more than 2^8: until then exp2 values stay
-    // below 256, and O and l keep a common, slightly stale reference, which divides out exactly.
+    for (int i = 4; i < 16; ++i) m4[i & 3] = fmaxf(fmaxf(m4[i & 3], sc[0][i]), sc[1][i]);
+    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    return partner32_max(mx) * c_log2;
+  };
+  // Rescale only when some row's maximum grew by more than 2^8: until then exp2 values stay
+  // below 256, and O and l keep a common, slightly stale reference, which divides out exactly.
+  auto raise_max = [&](float mx) {
     if (__ballot(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -527,19 +531,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
         for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
       m_run = m_new;
     }
-    // P^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t; the row
-    // sum adds the same bf16 values the PV product uses.
+  };
+  // P^T of the block (B operand of the PV product) and its row sum; key chunk c = 2 t + u takes
+  // elements 8u .. 8u+7 of tile t, and the row sum adds the same bf16 values the product uses.
+  // Then O^T += V^T P^T with V^T fragments read from the tile vt by transpose reads.
+  auto accumulate = [&](const f32x16 (&sc)[2], lchar* vt) {
     bf16x8 pb[4];
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial row sums
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t w0[4], w1[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
-        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
+        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e + 1], c_log2, -m_run)));
+        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e + 1], c_log2, -m_run)));
         rs[(e & 1) * 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs[(e & 1) * 2], false);
         rs[(e & 1) * 2 + 1] =
             __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs[(e & 1) * 2 + 1], false);
@@ -553,36 +560,73 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int r = 0; r < D / 32; ++r) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(cur + voff[r][0] + c * 16 * C::ROWB));
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(cur + voff[r][1] + c * 16 * C::ROWB));
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
         const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
       }
   };
 
-  using no_tail = std::integral_constant<bool, false>;
-  using tail = std::integral_constant<bool, true>;
-  const bool ragged_last = cnt > 0 && ragged && list[cnt - 1] == nkb - 1;
-  int t = 0;
-  for (; t + 2 < cnt; t += 2) {
-    iter(buf0, buf1, t, no_tail{});
-    iter(buf1, buf0, t + 1, no_tail{});
-  }
-  if (t + 1 < cnt) {
-    iter(buf0, buf1, t, no_tail{});
-    if (ragged_last) iter(buf1, buf0, t + 1, tail{});
-    else iter(buf1, buf0, t + 1, no_tail{});
-  } else if (t < cnt) {
-    if (ragged_last) iter(buf0, buf1, t, tail{});
-    else iter(buf0, buf1, t, no_tail{});
+  const bool ragged_last = cnt > 0 && (N % BK) != 0 && blk(cnt - 1) == nkb - 1;
+  // Step t. NEXT: 0 = no block t + 1 (last step), 1 = full block t + 1, 2 = ragged block t + 1.
+  // kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1).
+  auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
+                  auto next_tag) {
+    constexpr int NEXT = decltype(next_tag)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
+    if (t + 2 < cnt) dma_tile<D, BQ>(kbase, blk(t + 2), N, wave, lane, doff, kf);
+    if (t + 1 < cnt) dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, vf);
+    if constexpr (NEXT != 0) {
+      scores(kn, sn);
+      if constexpr (NEXT == 2) mask_tail(sn, blk(t + 1));
+    }
+    accumulate(sc, vc);
+    if constexpr (NEXT != 0) raise_max(block_max(sn));
+  };
+
+  using last = std::integral_constant<int, 0>;
+  using full = std::integral_constant<int, 1>;
+  using rag = std::integral_constant<int, 2>;
+  if (cnt > 0) {
+    f32x16 sa[2], sb[2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    scores(kb0, sa);
+    if (ragged_last && cnt == 1) mask_tail(sa, blk(0));
+    raise_max(block_max(sa));
+    // steps whose next block is a full one, unrolled by two so that S alternates between sa
+    // and sb and the buffers between their even / odd roles without copies
+    const int nfull = ragged_last ? cnt - 2 : cnt - 1;
+    int t = 0;
+    for (; t + 1 < nfull; t += 2) {
+      step(t, sa, sb, kb1, vb0, kb0, vb1, full{});
+      step(t + 1, sb, sa, kb0, vb1, kb1, vb0, full{});
+    }
+    if (t < nfull) {
+      step(t, sa, sb, kb1, vb0, kb0, vb1, full{});
+      ++t;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+    }
+    // at most two steps remain: one whose next block is the ragged last block, and the last one
+    const bool odd = (t & 1) != 0;
+    if (t + 1 < cnt) {
+      step(t, sa, sb, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1, rag{});
+      ++t;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+    }
+    const bool odd2 = (t & 1) != 0;
+    step(t, sa, sb, odd2 ? kb0 : kb1, odd2 ? vb1 : vb0, odd2 ? kb1 : kb0, odd2 ? vb0 : vb1, last{});
   }
   __syncthreads();
 
-  // epilogue: O = O^T / l, staged through LDS (two waves per buffer) for row-contiguous stores
+  // epilogue: O = O^T / l, staged through LDS (two waves per buffer pair) for row-contiguous stores
   const float l_tot = partner32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  lchar* ol = ((wave & 1) ? buf1 : buf0) + (wave >> 1) * 32 * C::OROW;
+  lchar* ol = ((wave & 1) ? vb0 : kb0) + (wave >> 1) * 32 * C::OROW;
 #pragma unroll
   for (int r = 0; r < D / 32; ++r)
 #pragma unroll
@@ -603,7 +647,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       *reinterpret_cast<u32x4*>(obase + (size_t)qr * D * 2 + cc * 16) =
           *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ol + r * C::OROW + cc * 16);
   }
-  if (lse != nullptr && hf == 0 && qrow < N) {
+  if (lse != nullptr && hf == 0 && qvalid) {
     lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 }
@@ -616,14 +660,17 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
 }
 
 template <int DT, int D, int BQ>
-static void launch_attn_t(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
-                          int BH, int N, int nqb, int nkb, float c_log2, void* o, float* lse, hipStream_t stream) {
-  if constexpr (DT == kBF16)
+static hipError_t launch_attn_t(const void* q, const void* k, const void* v, const int32_t* kidx,
+                                const int32_t* kcnt, int BH, int N, int nqb, int nkb, float c_log2, void* o,
+                                float* lse, hipStream_t stream) {
+  if constexpr (DT == kBF16) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
                        q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
-  else
+  } else {
     hipLaunchKernelGGL((attn_fwd_staged_kernel<DT, D, BQ>), dim3((unsigned)(BH * nqb)), dim3(AttnCfg<DT, D, BQ>::NT),
                        0, stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
@@ -632,11 +679,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, c
   const int nqb = (N + Bq - 1) / Bq;
   const int nkb = (N + BK - 1) / BK;
   const float c_log2 = (float)(scale * 1.4426950408889634);
-#define SA_ATTN_CASE(DT_, D_, BQ_)                                                                  \
-  if (dtype == DT_ && d == D_ && Bq == BQ_) {                                                     \
-    launch_attn_t<DT_, D_, BQ_>(q, k, v, kidx, kcnt, BH, N, nqb, nkb, c_log2, o, lse, stream);    \
-    return hipGetLastError();                                                                       \
-  }
+#define SA_ATTN_CASE(DT_, D_, BQ_)                                                               \
+  if (dtype == DT_ && d == D_ && Bq == BQ_)                                                      \
+    return launch_attn_t<DT_, D_, BQ_>(q, k, v, kidx, kcnt, BH, N, nqb, nkb, c_log2, o, lse, stream);
   SA_ATTN_CASE(kBF16, 128, 128)
   SA_ATTN_CASE(kBF16, 128, 64)
   SA_ATTN_CASE(kBF16, 64, 128)

@@ -125,7 +125,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, cons
  *   kept_idx    device, [B, H, nQB, nKB] int32: row r walks kept_idx[r][0 .. kept_cnt[r]-1].
  *   kept_cnt    device, [B, H, nQB] int32.
  * Entries are expected ascending in [0, nKB) and counts in [0, nKB]. The kernel clamps counts
- * to that range and never reads K/V outside [0, N); other bad entries give unspecified values.
+ * and entries to those ranges and never reads K/V outside [0, N); other bad entries give
+ * unspecified values.
  * The remaining arguments are those of sparse_attn_fwd.
  */
 int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,

@@ -206,3 +206,40 @@ def test_density_sweep(k_frac):
     want = oracle.topk_count(k_frac, m.shape[-1])
     assert torch.all(m.sum(-1, dtype=torch.int64) == want).item()
     check_attention(q, k, v, m, w.bq, w.bk, blocks=sample_blocks(w, x, [3, 30], per_head_random=2, seed=1))
+
+
+def test_lists_path_matches_mask_path():
+    """fwd_lists (the call the benchmark times) on the kept lists of select_mask gives the same
+    bits as fwd on the mask, on the full 720p-shaped workload."""
+    w, x, (q, k, v) = workload_inputs("wan720p")
+    qp, kp = sa.pool_qk(q, k, w.bq, w.bk)
+    sel = sa.select_mask(qp, kp, w.k_frac, w.p, kept_lists=True)
+    o1, l1 = sa.fwd(q, k, v, sel["mask"], w.bq, w.bk, return_lse=True)
+    o2, l2 = sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_lists_out_of_range_entries_are_clamped(dt):
+    """Entries outside [0, nKB) and counts above nKB are clamped: the call completes, reads
+    nothing outside K and V, and rows whose entries are all valid are unaffected."""
+    B, H, N, d, bq, bk = 1, 2, 1000, 128, 128, 64
+    q, k, v = (t.to(DEV) for t in rand_qkv(B, H, N, d, dt, 11))
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    idx = torch.arange(nkb, dtype=torch.int32).repeat(B, H, nqb, 1)
+    cnt = torch.full((B, H, nqb), nkb, dtype=torch.int32)
+    idx[0, 0, 1, :3] = torch.tensor([-7, 1 << 20, nkb], dtype=torch.int32)
+    cnt[0, 1, 2] = 1 << 20
+    cnt[0, 1, 3] = -4
+    o = sa.fwd_lists(q, k, v, idx.to(DEV), cnt.to(DEV), bq, bk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    full = torch.ones((B, H, nqb, nkb), dtype=torch.uint8, device=DEV)
+    ref = sa.fwd(q, k, v, full, bq, bk)
+    good = torch.ones((H, nqb), dtype=torch.bool)
+    good[0, 1] = False
+    good[1, 3] = False
+    rows = good.repeat_interleave(bq, dim=1)[:, :N]
+    assert torch.equal(o[0][rows.to(DEV)], ref[0][rows.to(DEV)])
+    assert torch.equal(o[0, 1, 3 * bq:4 * bq], torch.zeros_like(o[0, 1, 3 * bq:4 * bq]))  # count -4 -> empty row
