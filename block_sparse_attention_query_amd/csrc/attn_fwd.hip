@@ -576,12 +576,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     constexpr int NEXT = decltype(next_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
-    if (t + 2 < cnt) dma_tile<D, BQ>(kbase, blk(t + 2), N, wave, lane, doff, kf);
-    if (t + 1 < cnt) dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, vf);
+    // the DMA for K(t+2) and V(t+1) is issued behind the score MFMAs, so that the waves released
+    // by the barrier start on the matrix cores instead of queueing their copies first
+    const int blk2 = t + 2 < cnt ? blk(t + 2) : -1;
+    const int blk1 = t + 1 < cnt ? blk(t + 1) : -1;
     if constexpr (NEXT != 0) {
       scores(kn, sn);
-      if constexpr (NEXT == 2) mask_tail(sn, blk(t + 1));
+      if constexpr (NEXT == 2) mask_tail(sn, blk1);
     }
+    if (blk2 >= 0) dma_tile<D, BQ>(kbase, blk2, N, wave, lane, doff, kf);
+    if (blk1 >= 0) dma_tile<D, BQ>(vbase, blk1, N, wave, lane, doff, vf);
     accumulate(sc, vc);
     if constexpr (NEXT != 0) raise_max(block_max(sn));
   };
