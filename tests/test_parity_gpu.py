@@ -243,3 +243,35 @@ def test_lists_out_of_range_entries_are_clamped(dt):
     rows = good.repeat_interleave(bq, dim=1)[:, :N]
     assert torch.equal(o[0][rows.to(DEV)], ref[0][rows.to(DEV)])
     assert torch.equal(o[0, 1, 3 * bq:4 * bq], torch.zeros_like(o[0, 1, 3 * bq:4 * bq]))  # count -4 -> empty row
+
+
+@pytest.mark.parametrize("nkb,k_frac,p", [(2048, 0.03, 0.9), (2049, 0.03, 0.9), (3000, 0.1, 0.5),
+                                          (8192, 0.01, 0.95)])
+def test_select_long_rows(nkb, k_frac, p):
+    """Rows of 2048 key blocks (the last size taken by one wave per row) and of 2049-8192 (one
+    workgroup per row), on synthetic pooled vectors with a smooth key profile plus sinks."""
+    B, H, nqb, d = 1, 2, 5, 64
+    g = torch.Generator().manual_seed(nkb)
+    base = torch.randn(B, H, 1, d, generator=g, dtype=torch.float64)
+    qp = base + 0.5 * torch.randn(B, H, nqb, d, generator=g, dtype=torch.float64)
+    t = torch.linspace(0, 6.283, nkb, dtype=torch.float64)
+    kp = 0.3 * torch.randn(B, H, nkb, d, generator=g, dtype=torch.float64) \
+        + torch.sin(t)[None, None, :, None] * base
+    kp[..., ::997, :] *= 4.0  # a few sinks
+    qp, kp = qp.to(DEV), kp.to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    sel = sa.select_mask(qp, kp, k_frac, p, scale, kept_lists=True)
+    probs = oracle.pooled_probabilities(f64(qp), f64(kp), scale)
+    ref, _ = oracle.select_mask(probs, k_frac, p)
+    np.testing.assert_allclose(f64(sel["probs"]), probs, rtol=0, atol=1e-13)
+    gm = sel["mask"].cpu().numpy()
+    rep = oracle.compare_masks(probs, ref, gm, k_frac, p)
+    print(f"  nkb={nkb} rows={rep['rows']} equal={rep['rows_equal']} ties={rep['ties']} "
+          f"mismatches={rep['mismatches']} kept/row={gm.sum(-1).mean():.1f}", flush=True)
+    assert rep["mismatches"] == 0, rep["mismatch_rows"]
+    cnt = sel["kept_cnt"].cpu().numpy().reshape(-1)
+    idx = sel["kept_idx"].cpu().numpy().reshape(-1, nkb)
+    flat = gm.reshape(-1, nkb)
+    np.testing.assert_array_equal(cnt, flat.sum(-1))
+    for r in range(flat.shape[0]):
+        np.testing.assert_array_equal(idx[r, :cnt[r]], np.nonzero(flat[r])[0])
