@@ -39,15 +39,16 @@ def attn_source_digest() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per attention launch from committed rocprofv3 counters, if still current."""
+    """HBM bytes per attention launch and its L2 hit rate, from committed rocprofv3 counters, if
+    they were taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if rec.get("source_sha256") != attn_source_digest():
-        return None
-    return rec.get("bytes_per_launch")
+        return None, None
+    return rec.get("bytes_per_launch"), rec.get("l2_hit_rate")
 
 
 def executed_flops(mask_cpu, n, bq, bk, d):
@@ -64,18 +65,25 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
     import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        blas_threads = 1
+        blas_threads, threadpool_limits = 1, None
     h = 0
     q = x["q"][:, h:h + 1].double().numpy()
     k = x["k"][:, h:h + 1].double().numpy()
     v = x["v"][:, h:h + 1].double().numpy()
     nqb = mask_cpu.shape[2]
+    scale = 1.0 / math.sqrt(w.head_dim)
     t0 = time.perf_counter()
-    mask_o, _ = oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, 1.0 / math.sqrt(w.head_dim))
+    mask_o, _ = oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, scale)
     t_mask = time.perf_counter() - t0
+    t_mask_1t = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, scale)
+            t_mask_1t = time.perf_counter() - t0
     blocks = sorted(set(np.linspace(0, nqb - 1, sample_blocks).round().astype(int).tolist()))
     t0 = time.perf_counter()
     oracle.masked_attention(q, k, v, mask_o, w.bq, w.bk, blocks=[(0, 0, i) for i in blocks])
@@ -84,6 +92,9 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
     sub[0, 0, blocks] = mask_o[0, 0, blocks]
     flops = oracle.executed_flops(sub, w.tokens, w.bq, w.bk, w.head_dim)
     t = t_attn + t_mask * len(blocks) / nqb
+    # whole call on all heads: the mask oracle per head, attention scaled by executed FLOPs
+    full_flops = executed_flops(mask_cpu, w.tokens, w.bq, w.bk, w.head_dim)
+    extrapolated = w.batch * w.heads * t_mask + t_attn * full_flops / flops
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
@@ -93,21 +104,114 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
                    f"prorated to the sample), masked-dense attention on {len(blocks)} evenly spaced query "
                    f"blocks ({t_attn:.2f} s); executed FLOPs of those blocks / time"),
         "host_cpus": len(os.sched_getaffinity(0)),
-        "seconds": round(t_mask + t_attn, 2),
+        "seconds": round(t_mask + t_attn + (t_mask_1t or 0.0), 2),
+        "mask_oracle_head_s": round(t_mask, 3),
+        "mask_oracle_head_s_1thread": None if t_mask_1t is None else round(t_mask_1t, 3),
+        "extrapolated_full_call_s": round(extrapolated, 1),
+        "extrapolated_note": "extrapolated, not measured: mask oracle time x all heads + sampled attention "
+                             "time scaled by executed FLOPs of the whole call",
+    }
+
+
+def pattern_bench(args, sa, w, q, k, v, gen_s):
+    """Fixed-pattern workloads on the same kernel. The masks depend on positions only, so they are
+    built once before the timed region; a step is the attention work of the pattern."""
+    import numpy as np
+    import torch
+    B, H, N, d = q.shape
+    frame = w.grid[1] * w.grid[2]
+    o = torch.empty_like(q)
+    if args.pattern == "squad":
+        window = 3 * w.grid[2]  # 3 latent rows: 240 tokens at 720p, about sqrt(N)
+        masks = sa.squad_masks(B, H, N, window, w.bq, w.bk, q.device)
+        bufs = [torch.empty_like(q) for _ in range(4)]
+        names = ["window_transpose", "fwd_lists"]
+
+        def step(ev):
+            ml, mg = masks
+            ev[0].record()
+            sa.fwd_lists(q, k, v, ml["kept_idx"], ml["kept_cnt"], w.bq, w.bk, out=bufs[0])   # local pass
+            ev[1].record()
+            sa.window_transpose(q, window, out=bufs[1])
+            sa.window_transpose(k, window, out=bufs[2])
+            sa.window_transpose(bufs[0], window, out=bufs[3])
+            ev[2].record()
+            sa.fwd_lists(bufs[1], bufs[2], bufs[3], mg["kept_idx"], mg["kept_cnt"], w.bq, w.bk, out=bufs[0])
+            ev[3].record()
+            sa.window_transpose(bufs[0], window, inverse=True, out=o)
+            ev[4].record()
+
+        mask_list = [m["mask"].cpu().numpy() for m in masks]
+        params = {"window": window, "global_run": N // window}
+        split = lambda e: (e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]),  # noqa: E731
+                           e[1].elapsed_time(e[2]) + e[3].elapsed_time(e[4]))
+        metric = "SQuad two-pass (local + global) sparse attention fwd TFLOP/s (executed)"
+    else:
+        band, period = 3 * w.grid[2], frame
+        m = sa.pattern_mask(sa.SA_PAT_DIAG | sa.SA_PAT_MULTIDIAG | sa.SA_PAT_STRIPE, B, H, N, w.bq, w.bk,
+                            band=band, period=period, device=q.device)
+
+        def step(ev):
+            ev[0].record()
+            sa.fwd_lists(q, k, v, m["kept_idx"], m["kept_cnt"], w.bq, w.bk, out=o)
+            ev[1].record()
+
+        mask_list = [m["mask"].cpu().numpy()]
+        params = {"band": band, "period": period, "stripe_period": period}
+        split = lambda e: (e[0].elapsed_time(e[1]), 0.0)  # noqa: E731
+        metric = "Sparse-vDiT pattern (diagonal + per-frame diagonals + frame-start stripes) sparse attention fwd " \
+                 "TFLOP/s (executed)"
+    flops = sum(executed_flops(mm, N, w.bq, w.bk, d) for mm in mask_list)
+    nev = 5 if args.pattern == "squad" else 2
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(nev)])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for e in evs:
+        step(e)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    attn_ms, perm_ms = (float(v) for v in np.array([split(e) for e in evs]).mean(axis=0))
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": metric, "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {args.pattern} fixed pattern on the {w.grid[0]}x{w.grid[1]}x{w.grid[2]} "
+                               f"latent grid", "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq,
+                   "bk": w.bk, **params,
+                   "kept_block_density": [round(float(mm.mean()), 5) for mm in mask_list],
+                   "executed_tflop_per_step": round(flops / 1e12, 4), "masks": "built once, outside the timed region",
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_call": {"fwd_lists_total": round(attn_ms, 4), "window_transpose_total": round(perm_ms, 4)},
+        "roofline": {"kernel": "attn_fwd_kernel<bf16, 128, 128>", "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "window_transpose_gbs": None if perm_ms == 0 else round(4 * 2 * B * H * N * d * q.element_size()
+                                                                / (perm_ms * 1e-3) / 1e9, 1),
+        "input_generation_s": round(gen_s, 1),
     }
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=240)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps times (to calibrate "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a known byte count) and exit")
+    ap.add_argument("--pattern", choices=("hybrid", "squad", "vdit"), default="hybrid",
+                    help="hybrid: the Top-k U Top-p path (default). squad: fixed two-pass SQuad attention (local "
+                         "windows of 240 tokens, then the same-position pass in the window-transposed order). "
+                         "vdit: Sparse-vDiT style union of a diagonal band, the band repeated every frame and the "
+                         "first key token of every frame")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -147,6 +251,9 @@ def main(argv=None):
            "kept_idx": torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=dev),
            "kept_cnt": torch.empty((B, H, nqb), dtype=torch.int32, device=dev)}
     o = torch.empty_like(q)
+    if args.pattern != "hybrid":
+        print(json.dumps(pattern_bench(args, sa, w, q, k, v, gen_s)), flush=True)
+        return 0
 
     def step(ev=None):
         if ev is not None:
@@ -166,6 +273,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     mask_cpu = sel["mask"].cpu().numpy()
     flops = executed_flops(mask_cpu, N, w.bq, w.bk, d)
+    tile_flops = 4.0 * d * w.bq * w.bk * float(mask_cpu.sum())  # what the kernel runs, padding included
     density = float(mask_cpu.mean())
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -180,9 +288,13 @@ def main(argv=None):
     ms_step = total_ms / args.steps
     per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
     pool_ms, select_ms, attn_ms = (float(v) for v in per.mean(axis=0))
+    stats = {name: {"median": round(float(np.median(col)), 4), "p10": round(float(np.percentile(col, 10)), 4),
+                    "p90": round(float(np.percentile(col, 90)), 4)}
+             for name, col in zip(("pool_qk", "select_mask", "fwd_lists"), per.T)}
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    alg_bytes = 4 * B * H * N * d * q.element_size()  # Q, K, V read once and O written once
+    traffic, l2_hit = measured_traffic()
     result = {
         "metric": "sparse attention fwd TFLOP/s (executed) + ms/call at 95% sparsity; % bf16 MFMA peak",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -203,11 +315,14 @@ def main(argv=None):
                    "parallelism": "none (1 GPU)"},
         "ms_per_call": {"pool_qk": round(pool_ms, 4), "select_mask": round(select_ms, 4),
                         "fwd_lists": round(attn_ms, 4)},
+        "ms_per_call_stats": stats,
+        "tile_tflop_per_step": round(tile_flops / 1e12, 4),
         "fwd_tflops": round(attn_tflops, 2),
         "fwd_pct_bf16_peak": round(100 * attn_tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": {"kernel": "attn_fwd_kernel<bf16, 128, 128>", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes, "l2_hit_rate": l2_hit},
         "pool_gbs": round(2 * B * H * N * d * q.element_size() / (pool_ms * 1e-3) / 1e9, 1),
         "input_generation_s": round(gen_s, 1),
     }

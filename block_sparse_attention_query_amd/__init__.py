@@ -17,9 +17,11 @@ import math
 import torch
 
 from . import _lib
-from ._lib import SA_BF16, SA_F32, SparseAttnError  # noqa: F401
+from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA_PAT_MULTIDIAG,  # noqa: F401
+                   SA_PAT_STRIPE, SparseAttnError)
 
-__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "topk_count", "sparse_attention",
+__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "pattern_mask",
+           "window_transpose", "squad_attention", "topk_count", "sparse_attention",
            "SparseAttnError"]
 
 _DTYPES = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}
@@ -165,3 +167,59 @@ def sparse_attention(q, k, v, bq: int, bk: int, k_frac: float, p: float, scale: 
     qp, kp = pool_qk(q, k, bq, bk)
     sel = select_mask(qp, kp, k_frac, p, scale)
     return fwd(q, k, v, sel["mask"], bq, bk, scale), sel["mask"]
+
+
+def pattern_mask(patterns: int, B: int, H: int, N: int, bq: int, bk: int = 64, window: int = 0, band: int = 0,
+                 period: int = 0, kept_lists: bool = True, device="cuda", out: dict | None = None):
+    """Block mask (and kept lists) of a union of fixed patterns (SA_PAT_* flags)."""
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    dev = torch.device(device)
+    out = {} if out is None else out
+    mask = out.get("mask")
+    if mask is None:
+        mask = out["mask"] = torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=dev)
+    else:
+        _check_out(mask, (B, H, nqb, nkb), torch.uint8, dev)
+    idx_ptr = cnt_ptr = None
+    if kept_lists:
+        if out.get("kept_idx") is None:
+            out["kept_idx"] = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=dev)
+            out["kept_cnt"] = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
+        idx_ptr, cnt_ptr = out["kept_idx"].data_ptr(), out["kept_cnt"].data_ptr()
+    _lib.check(_lib.lib().sparse_attn_pattern_mask(int(patterns), int(window), int(band), int(period), B, H, N, bq,
+                                                   bk, mask.data_ptr(), idx_ptr, cnt_ptr, _stream(mask)))
+    return out
+
+
+def window_transpose(x: torch.Tensor, window: int, inverse: bool = False, out: torch.Tensor | None = None):
+    """Token-axis window transpose of a [B, H, N, d] tensor (the tokens at one position inside
+    their window become contiguous; ``inverse`` undoes it)."""
+    _check_qkv(x)
+    B, H, N, d = x.shape
+    o = torch.empty_like(x) if out is None else _check_out(out, x.shape, x.dtype, x.device)
+    _lib.check(_lib.lib().sparse_attn_window_transpose(x.data_ptr(), _DTYPES[x.dtype], B, H, N, d, int(window),
+                                                       int(bool(inverse)), o.data_ptr(), _stream(x)))
+    return o
+
+
+def squad_masks(B: int, H: int, N: int, window: int, bq: int, bk: int = 64, device="cuda"):
+    """Kept lists of the two SQuad passes: the local pass in raster order and, in the
+    window-transposed order, the local pass over runs of N / window tokens (the global pass)."""
+    if window <= 0 or N % window:
+        raise ValueError("the window must divide N")
+    return (pattern_mask(SA_PAT_LOCAL, B, H, N, bq, bk, window=window, device=device),
+            pattern_mask(SA_PAT_LOCAL, B, H, N, bq, bk, window=N // window, device=device))
+
+
+def squad_attention(q, k, v, window: int, bq: int, bk: int = 64, scale: float | None = None, masks=None,
+                    return_local: bool = False):
+    """Two-pass SQuad attention on the block-sparse kernel: O_local = attention with the local
+    mask; then, in the window-transposed token order, attention of (Q, K, O_local) with the global
+    mask, permuted back to raster order."""
+    B, H, N, d = q.shape
+    ml, mg = squad_masks(B, H, N, window, bq, bk, q.device) if masks is None else masks
+    o_local = fwd_lists(q, k, v, ml["kept_idx"], ml["kept_cnt"], bq, bk, scale)
+    qt, kt, vt = (window_transpose(t, window) for t in (q, k, o_local))
+    ot = fwd_lists(qt, kt, vt, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale)
+    o = window_transpose(ot, window, inverse=True)
+    return (o, o_local) if return_local else o

@@ -13,6 +13,7 @@ SA_ERR_UNSUPPORTED = -2
 SA_ERR_HIP = -3
 SA_BF16 = 0
 SA_F32 = 1
+SA_PAT_LOCAL, SA_PAT_GLOBAL, SA_PAT_DIAG, SA_PAT_MULTIDIAG, SA_PAT_STRIPE = 1, 2, 4, 8, 16
 
 # Every symbol include/sparse_attn.h declares, with (restype, argtypes).
 _vp, _i, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
@@ -22,6 +23,8 @@ SIGNATURES = {
     "sparse_attn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_fwd": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_fwd_lists": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
+    "sparse_attn_pattern_mask": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "sparse_attn_window_transpose": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "sparse_attn_topk_count": (_i, [_d, _i]),
     "sparse_attn_error_string": (ctypes.c_char_p, [_i]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),

@@ -20,6 +20,10 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
                        const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
                        hipStream_t stream);
+hipError_t launch_pattern_mask(int kinds, int window, int band, int period, int BH, int N, int Bq, int Bk,
+                               uint8_t* mask, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
+hipError_t launch_window_transpose(const void* x, void* out, int BH, int N, int row_bytes, int w, int inverse,
+                                   hipStream_t stream);
 }  // namespace sa
 
 namespace {
@@ -182,6 +186,48 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, cons
   if (rc) return rc;
   return hip_status(sa::launch_attn(q, k, v, dtype, kidx, kcnt, B * H, N, d, Bq, scale, o, lse, s),
                     "fwd: attention launch");
+}
+
+int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int B, int H, int N, int Bq, int Bk,
+                             uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
+  if (!mask) return fail(SA_ERR_INVALID_ARG, "pattern_mask: null mask");
+  if ((kept_idx == nullptr) != (kept_cnt == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "pattern_mask: kept_idx and kept_cnt must both be given or both be NULL");
+  if (B <= 0 || H <= 0 || N <= 0) return fail(SA_ERR_INVALID_ARG, "pattern_mask: B, H and N must be positive");
+  if ((long long)B * H > 65535) return fail(SA_ERR_UNSUPPORTED, "pattern_mask: B*H exceeds 65535");
+  if ((Bq != 64 && Bq != 128) || (Bk != 64 && Bk != 128))
+    return fail(SA_ERR_UNSUPPORTED, "pattern_mask: block sizes Bq=%d Bk=%d not in {64, 128}", Bq, Bk);
+  if (patterns <= 0 || (patterns & ~(SA_PAT_LOCAL | SA_PAT_GLOBAL | SA_PAT_DIAG | SA_PAT_MULTIDIAG | SA_PAT_STRIPE)))
+    return fail(SA_ERR_INVALID_ARG, "pattern_mask: pattern set 0x%x is empty or has unknown bits", patterns);
+  if ((patterns & (SA_PAT_LOCAL | SA_PAT_GLOBAL)) && window <= 0)
+    return fail(SA_ERR_INVALID_ARG, "pattern_mask: window must be positive");
+  if ((patterns & (SA_PAT_DIAG | SA_PAT_MULTIDIAG)) && band < 0)
+    return fail(SA_ERR_INVALID_ARG, "pattern_mask: band must be >= 0");
+  if ((patterns & (SA_PAT_MULTIDIAG | SA_PAT_STRIPE)) && period <= 0)
+    return fail(SA_ERR_INVALID_ARG, "pattern_mask: period must be positive");
+  const int nkb = cdiv(N, Bk);
+  if (nkb > SA_MAX_NKB) return fail(SA_ERR_UNSUPPORTED, "pattern_mask: nkb=%d exceeds %d", nkb, SA_MAX_NKB);
+  if ((long long)B * H * cdiv(N, Bq) > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "pattern_mask: too many rows");
+  return hip_status(sa::launch_pattern_mask(patterns, window > 0 ? window : 1, band, period > 0 ? period : 1, B * H,
+                                            N, Bq, Bk, mask, kept_idx, kept_cnt, static_cast<hipStream_t>(stream)),
+                    "pattern_mask launch");
+}
+
+int sparse_attn_window_transpose(const void* x, int dtype, int B, int H, int N, int d, int window, int inverse,
+                                 void* out, void* stream) {
+  if (!x || !out) return fail(SA_ERR_INVALID_ARG, "window_transpose: null pointer");
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if (window <= 0 || N % window != 0)
+    return fail(SA_ERR_INVALID_ARG, "window_transpose: window %d must be positive and divide N = %d", window, N);
+  if (x == out) return fail(SA_ERR_INVALID_ARG, "window_transpose: out must not alias x");
+  if (!aligned16(x) || !aligned16(out)) return fail(SA_ERR_INVALID_ARG, "window_transpose: pointers must be 16-byte aligned");
+  const long long threads = (long long)B * H * N * (d * (dtype == SA_BF16 ? 2 : 4) / 16);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "window_transpose: tensor too large");
+  return hip_status(sa::launch_window_transpose(x, out, B * H, N, d * (dtype == SA_BF16 ? 2 : 4), window, inverse != 0,
+                                                static_cast<hipStream_t>(stream)),
+                    "window_transpose launch");
 }
 
 }  // extern "C"

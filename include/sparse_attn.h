@@ -133,6 +133,52 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
                           const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, double scale,
                           void* o, float* lse, void* stream);
 
+/*
+ * Fixed block patterns, as masks for sparse_attn_fwd (SQuad page "SQuad: Sub-Quadratic Attention
+ * Distillation for Efficient Video Generation" (gist.science), section "手法": local pass inside
+ * windows of w tokens, global pass among the tokens at the same position inside their window;
+ * Sparse-vDiT page "Sparse-vDiT: Unleashing the Power of Sparse Attention to Accelerate Video
+ * Diffusion Transformers" (aibr.jp), section "3. 中核となる技術的要素": diagonal, multi-diagonal
+ * and vertical-stripe patterns). Token-level rules, t a query token and u a key token:
+ *   SA_PAT_LOCAL      floor(t / window) == floor(u / window)
+ *   SA_PAT_GLOBAL     t mod window == u mod window
+ *   SA_PAT_DIAG       |t - u| <= band
+ *   SA_PAT_MULTIDIAG  |t - u - m * period| <= band for some integer m
+ *   SA_PAT_STRIPE     u mod period == 0
+ * `patterns` is an OR of these; a block pair is kept when any (query token, key token) pair of
+ * the two blocks satisfies any selected rule (the block cover of the token pattern).
+ */
+#define SA_PAT_LOCAL 1
+#define SA_PAT_GLOBAL 2
+#define SA_PAT_DIAG 4
+#define SA_PAT_MULTIDIAG 8
+#define SA_PAT_STRIPE 16
+
+/*
+ *   window, band, period   parameters of the selected rules (window > 0 for LOCAL / GLOBAL,
+ *                          band >= 0 for DIAG / MULTIDIAG, period > 0 for MULTIDIAG / STRIPE;
+ *                          ignored otherwise).
+ *   mask        device out, [B, H, nQB, nKB] uint8 (the same pattern for every b, h).
+ *   kept_idx    device out or NULL, [B, H, nQB, nKB] int32, ascending kept indices per row.
+ *   kept_cnt    device out or NULL (both or neither), [B, H, nQB] int32.
+ * Bq, Bk in {64, 128}; nKB <= SA_MAX_NKB.
+ */
+int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int B, int H, int N, int Bq, int Bk,
+                             uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
+ * Window transpose of the token axis, the permutation that turns the SQuad global pass into a
+ * local pass ([SQuad] "手法") and leaves attention unchanged once the output is permuted back
+ * ([SVG2] "2. 手法" A: permutation equivalence). With nw = N / window:
+ *   forward (inverse = 0):  out[b, h, s, :] = x[b, h, (s mod nw) * window + s / nw, :]
+ *   inverse (inverse != 0): out[b, h, t, :] = x[b, h, (t mod window) * nw + t / window, :]
+ * so the tokens at one position inside their window form contiguous runs of nw.
+ *   x, out   device, [B, H, N, d] of `dtype`, 16-byte aligned, not aliased.
+ * window must divide N.
+ */
+int sparse_attn_window_transpose(const void* x, int dtype, int B, int H, int N, int d, int window, int inverse,
+                                 void* out, void* stream);
+
 /* Host helper: the Top-k size for a fraction, as select_mask computes it (-1 if invalid). */
 int sparse_attn_topk_count(double k_frac, int nkb);
 

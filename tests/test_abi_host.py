@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -133,3 +133,33 @@ def test_last_error_names_the_problem():
     with pytest.raises(_lib.SparseAttnError) as ei:
         _lib.check(_fwd(d=80))
     assert ei.value.code == -2 and "80" in str(ei.value)
+
+
+def _pattern(**kw):
+    a = dict(patterns=1, window=128, band=0, period=0, B=1, H=2, N=1024, Bq=128, Bk=64, mask=P, idx=None, cnt=None,
+             stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_pattern_mask(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), -1), (dict(idx=P), -1), (dict(cnt=P), -1), (dict(N=0), -1), (dict(patterns=0), -1),
+    (dict(patterns=32), -1), (dict(window=0), -1), (dict(patterns=4, band=-1), -1), (dict(patterns=8, band=3), -1),
+    (dict(patterns=16, period=-2), -1), (dict(Bq=32), -2), (dict(Bk=256), -2), (dict(N=64 * 8193), -2),
+])
+def test_pattern_mask_rejects(kw, code):
+    assert _pattern(**kw) == code
+
+
+def _wt(**kw):
+    a = dict(x=P, dtype=0, B=1, H=2, N=1024, d=64, window=128, inverse=0, out=P + 4096, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_window_transpose(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(out=None), -1), (dict(window=0), -1), (dict(window=100), -1), (dict(out=P), -1),
+    (dict(x=P_ODD), -1), (dict(d=96), -2), (dict(dtype=3), -2),
+])
+def test_window_transpose_rejects(kw, code):
+    assert _wt(**kw) == code

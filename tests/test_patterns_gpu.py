@@ -1,0 +1,108 @@
+"""GPU parity of the fixed-pattern masks, the window transpose and the two-pass SQuad attention
+against the float64 oracle (oracle/patterns.py), through the C ABI."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_query_amd as sa
+import oracle
+from oracle import patterns as pt
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+O_MAX, O_MEAN = 2e-2, 5e-3
+
+# (patterns, window, band, period)
+PATTERNS = [
+    (pt.LOCAL, 240, 0, 0),
+    (pt.LOCAL, 100, 0, 0),
+    (pt.GLOBAL, 240, 0, 0),
+    (pt.GLOBAL, 37, 0, 0),
+    (pt.DIAG, 0, 0, 0),
+    (pt.DIAG, 0, 130, 0),
+    (pt.MULTIDIAG, 0, 50, 700),
+    (pt.MULTIDIAG, 0, 0, 333),
+    (pt.STRIPE, 0, 0, 300),
+    (pt.DIAG | pt.MULTIDIAG | pt.STRIPE, 0, 80, 1000),
+    (pt.LOCAL | pt.GLOBAL, 250, 0, 0),
+]
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+@pytest.mark.parametrize("n,bq,bk", [(3000, 128, 64), (2500, 64, 64), (1000, 128, 128), (77, 64, 64)])
+@pytest.mark.parametrize("pat", PATTERNS, ids=[f"p{p[0]}w{p[1]}b{p[2]}P{p[3]}" for p in PATTERNS])
+def test_pattern_mask_matches_brute_force(n, bq, bk, pat):
+    kinds, window, band, period = pat
+    sel = sa.pattern_mask(kinds, 1, 2, n, bq, bk, window=window, band=band, period=period, device=DEV)
+    ref = pt.pattern_block_mask(kinds, n, bq, bk, window=window, band=band, period=period)
+    gm = sel["mask"].cpu().numpy()
+    assert (gm == ref[None, None]).all()
+    cnt, idx = sel["kept_cnt"].cpu().numpy(), sel["kept_idx"].cpu().numpy()
+    for h in range(2):
+        for i in range(ref.shape[0]):
+            np.testing.assert_array_equal(idx[0, h, i, :cnt[0, h, i]], np.nonzero(ref[i])[0])
+
+
+@pytest.mark.parametrize("pat", [(pt.LOCAL, 240, 0, 0), (pt.GLOBAL, 240, 0, 0),
+                                 (pt.DIAG | pt.MULTIDIAG | pt.STRIPE, 0, 240, 3600)])
+def test_pattern_mask_720p_rows(pat):
+    """The 720p token count (21 x 45 x 80), sampled query blocks checked by brute force."""
+    kinds, window, band, period = pat
+    n, bq, bk = 75600, 128, 64
+    sel = sa.pattern_mask(kinds, 1, 1, n, bq, bk, window=window, band=band, period=period, device=DEV,
+                          kept_lists=False)
+    rows = [0, 1, 17, 295, 296, 589, 590]
+    ref = pt.pattern_block_mask(kinds, n, bq, bk, window=window, band=band, period=period, rows=rows)
+    gm = sel["mask"].cpu().numpy()[0, 0]
+    np.testing.assert_array_equal(gm[rows], ref[rows])
+    print(f"  pattern {kinds}: density {gm.mean():.4f}", flush=True)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,w", [(2048, 64), (1000, 40), (75600, 240)])
+def test_window_transpose_is_the_permutation(dt, n, w):
+    g = torch.Generator().manual_seed(n)
+    x = torch.randn(1, 2, n, 64, generator=g).to(dt).to(DEV)
+    y = sa.window_transpose(x, w)
+    perm = torch.from_numpy(pt.window_transpose(n, w)).to(DEV)
+    assert torch.equal(y, x[:, :, perm])
+    assert torch.equal(sa.window_transpose(y, w, inverse=True), x)
+
+
+@pytest.mark.parametrize("n,w,d,bq", [(2048, 64, 64, 128), (2048, 256, 128, 64), (1920, 240, 128, 128)])
+def test_squad_attention_matches_oracle(n, w, d, bq):
+    bk = 64
+    g = torch.Generator().manual_seed(w)
+    q, k, v = (torch.randn(1, 2, n, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    o, o_local = sa.squad_attention(q.to(DEV), k.to(DEV), v.to(DEV), w, bq, bk, return_local=True)
+    ro, rl = pt.squad_attention(f64(q), f64(k), f64(v), w, bq, bk, 1.0 / math.sqrt(d))
+    el = np.abs(f64(o_local) - rl)
+    e = np.abs(f64(o) - ro)
+    print(f"  squad n={n} w={w}: local max {el.max():.3e} mean {el.mean():.3e}; "
+          f"global max {e.max():.3e} mean {e.mean():.3e}", flush=True)
+    assert el.max() <= O_MAX and el.mean() <= O_MEAN
+    # the global pass reads the bf16-rounded local output as its values (relative 2^-9 each)
+    assert e.max() <= O_MAX and e.mean() <= O_MEAN
+
+
+def test_vdit_pattern_attention_matches_oracle():
+    """Sparse-vDiT style union (diagonal band, the same band every `period` tokens, and the first
+    key token of each period) through sparse_attn_fwd."""
+    n, d, bq, bk = 3000, 128, 128, 64
+    kinds, band, period = pt.DIAG | pt.MULTIDIAG | pt.STRIPE, 100, 1000
+    g = torch.Generator().manual_seed(9)
+    q, k, v = (torch.randn(1, 2, n, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    m = sa.pattern_mask(kinds, 1, 2, n, bq, bk, band=band, period=period, device=DEV, kept_lists=False)["mask"]
+    o, lse = sa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), m, bq, bk, return_lse=True)
+    ref_m = pt.pattern_block_mask(kinds, n, bq, bk, band=band, period=period)
+    ro, rl = oracle.masked_attention(f64(q), f64(k), f64(v), np.broadcast_to(ref_m, (1, 2) + ref_m.shape), bq, bk)
+    e = np.abs(f64(o) - ro)
+    assert e.max() <= O_MAX and e.mean() <= O_MEAN
+    assert np.all(np.abs(f64(lse) - rl) <= 1e-3 + math.log1p(2.0 ** -8))
