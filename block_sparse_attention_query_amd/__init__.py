@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA_PAT_MULTIDIAG,  # noqa: F401
                    SA_PAT_STRIPE, SparseAttnError)
 
-__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "pattern_mask",
+__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
+           "pattern_mask",
            "window_transpose", "squad_attention", "topk_count", "sparse_attention",
            "SparseAttnError"]
 
@@ -223,3 +224,36 @@ def squad_attention(q, k, v, window: int, bq: int, bk: int = 64, scale: float | 
     ot = fwd_lists(qt, kt, vt, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale)
     o = window_transpose(ot, window, inverse=True)
     return (o, o_local) if return_local else o
+
+
+def _workspace(nbytes: int, workspace, device):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace
+
+
+def bwd_workspace_size(B: int, H: int, N: int, bq: int, bk: int = 64) -> int:
+    return int(_lib.lib().sparse_attn_bwd_workspace_size(B, H, N, bq, bk))
+
+
+def bwd(q, k, v, o, dout, lse, mask, bq: int, bk: int = 64, scale: float | None = None,
+        workspace: torch.Tensor | None = None, out: tuple | None = None):
+    """(dQ, dK, dV) of the block-sparse attention for the forward's mask, output and LSE (bf16)."""
+    _check_qkv(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (B, H, nqb, nkb) or not mask.is_contiguous():
+        raise ValueError(f"mask must be a contiguous uint8 [{B}, {H}, {nqb}, {nkb}] tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 [{B}, {H}, {N}] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    workspace = _workspace(bwd_workspace_size(B, H, N, bq, bk), workspace, q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else \
+        (_check_out(t, q.shape, q.dtype, q.device) for t in out)
+    _lib.check(_lib.lib().sparse_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                          lse.data_ptr(), _DTYPES[q.dtype], mask.data_ptr(), B, H, N, d, bq, bk, scale,
+                                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv

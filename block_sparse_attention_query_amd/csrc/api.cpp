@@ -20,6 +20,10 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
                        const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
                        hipStream_t stream);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      const uint8_t* mask, int BH, int N, int d, int Bq, double scale, void* dq, void* dk, void* dv,
+                      void* ws, hipStream_t stream);
+size_t bwd_workspace_bytes(int BH, int N, int Bq);
 hipError_t launch_pattern_mask(int kinds, int window, int band, int period, int BH, int N, int Bq, int Bk,
                                uint8_t* mask, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
 hipError_t launch_window_transpose(const void* x, void* out, int BH, int N, int row_bytes, int w, int inverse,
@@ -186,6 +190,31 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, cons
   if (rc) return rc;
   return hip_status(sa::launch_attn(q, k, v, dtype, kidx, kcnt, B * H, N, d, Bq, scale, o, lse, s),
                     "fwd: attention launch");
+}
+
+size_t sparse_attn_bwd_workspace_size(int B, int H, int N, int Bq, int Bk) {
+  if (B <= 0 || H <= 0 || N <= 0 || (Bq != 64 && Bq != 128) || Bk != 64) return 0;
+  return sa::bwd_workspace_bytes(B * H, N, Bq);
+}
+
+int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    int dtype, const uint8_t* mask, int B, int H, int N, int d, int Bq, int Bk, double scale, void* dq,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!o || !dout || !lse || !mask || !dq || !dk || !dv || !workspace) return fail(SA_ERR_INVALID_ARG, "bwd: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, dq);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "bwd: only SA_BF16 tensors are supported");
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv))
+    return fail(SA_ERR_INVALID_ARG, "bwd: o, dout, dk and dv must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(SA_ERR_INVALID_ARG, "bwd: workspace must be 256-byte aligned");
+  const size_t need = sparse_attn_bwd_workspace_size(B, H, N, Bq, Bk);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_INVALID_ARG, "bwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if ((long long)B * H * cdiv(N, Bk) > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "bwd: too many key blocks");
+  return hip_status(sa::launch_bwd(q, k, v, o, dout, lse, mask, B * H, N, d, Bq, scale, dq, dk, dv, workspace,
+                                   static_cast<hipStream_t>(stream)),
+                    "bwd launch");
 }
 
 int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int B, int H, int N, int Bq, int Bk,

@@ -133,6 +133,30 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
                           const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, double scale,
                           void* o, float* lse, void* stream);
 
+/* Bytes of device workspace sparse_attn_bwd needs (row and column kept lists with counts, the
+ * transposed mask, and one float per query; each part 256-byte aligned). 0 for invalid shapes. */
+size_t sparse_attn_bwd_workspace_size(int B, int H, int N, int Bq, int Bk);
+
+/*
+ * Gradients of sparse_attn_fwd for the same mask (the sparse student of [SA2]
+ * "ハイブリッドマスキングと蒸留微調整" is fine-tuned by distillation). With s = scale * Q K^T over the
+ * kept keys, P = exp(s - LSE) and D = rowsum(dO * O):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v, o, dout  device, [B, H, N, d] SA_BF16 (o is the forward's output, dout the
+ *                     upstream gradient); `dtype` must be SA_BF16.
+ *   lse         device, [B, H, N] float32, the LSE the forward wrote for this mask.
+ *   mask        device, [B, H, nQB, nKB] uint8, the forward's mask.
+ *   dq, dk, dv  device out, [B, H, N, d] bf16 (fp32 accumulation). Queries of a block with no
+ *               kept key get dQ = 0; keys of a block no query block keeps get dK = dV = 0.
+ *   workspace   device scratch of at least sparse_attn_bwd_workspace_size() bytes, 256-byte
+ *               aligned; overwritten.
+ * Each output element is written by one workgroup in a fixed order (no atomics): repeated calls
+ * give identical bits. d in {64, 128}, Bq in {64, 128}, Bk = 64.
+ */
+int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    int dtype, const uint8_t* mask, int B, int H, int N, int d, int Bq, int Bk, double scale, void* dq,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Fixed block patterns, as masks for sparse_attn_fwd (SQuad page "SQuad: Sub-Quadratic Attention
  * Distillation for Efficient Video Generation" (gist.science), section "手法": local pass inside

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -163,3 +163,31 @@ def _wt(**kw):
 ])
 def test_window_transpose_rejects(kw, code):
     assert _wt(**kw) == code
+
+
+def _bwd(**kw):
+    ws = _lib.lib().sparse_attn_bwd_workspace_size(1, 2, 1024, 64, 64)
+    a = dict(q=P, k=P, v=P, o=P, g=P, lse=P, dtype=0, mask=P, B=1, H=2, N=1024, d=64, Bq=64, Bk=64, scale=0.125,
+             dq=P, dk=P, dv=P, ws=P, ws_bytes=ws, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), -1), (dict(g=None), -1), (dict(lse=None), -1), (dict(mask=None), -1), (dict(dk=None), -1),
+    (dict(ws=None), -1), (dict(ws_bytes=64), -1), (dict(ws=P + 16), -1), (dict(dv=P_ODD), -1), (dict(dtype=1), -2),
+    (dict(d=32), -2), (dict(Bk=128), -2), (dict(scale=0.0), -1),
+])
+def test_bwd_rejects(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_workspace_size():
+    lib = _lib.lib()
+    bh, n, bq = 2, 1000, 128
+    nqb, nkb = 8, 16
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = al(bh * nqb * nkb * 4) + al(bh * nqb * 4) + al(bh * nkb * nqb * 4) + al(bh * nkb * 4) + \
+        al(bh * nkb * nqb) + al(bh * n * 4)
+    assert lib.sparse_attn_bwd_workspace_size(1, 2, n, bq, 64) == want
+    assert lib.sparse_attn_bwd_workspace_size(1, 2, n, 96, 64) == 0

@@ -134,3 +134,35 @@ def test_planted_mistakes_are_caught(monkeypatch, kind):
     monkeypatch.setattr(bw, "masked_attention_bwd", _mutant(kind))
     with pytest.raises(AssertionError):
         check_against_autograd()
+
+
+def test_sampled_blocks_equal_full():
+    n, d, bq, bk = 130, 8, 32, 16
+    q, k, v, g = _inputs(1, 2, n, d, 21)
+    rng = np.random.default_rng(22)
+    mask = (rng.random((1, 2, oracle.num_blocks(n, bq), oracle.num_blocks(n, bk))) < 0.5).astype(np.uint8)
+    full = bw.masked_attention_bwd(q, k, v, mask, g, bq, bk)
+    qs, ks = [(0, 1, 2), (0, 0, 4)], [(0, 0, 3), (0, 1, 8), (0, 1, 0)]
+    part = bw.masked_attention_bwd(q, k, v, mask, g, bq, bk, q_blocks=qs, k_blocks=ks)
+    for (b, h, i) in qs:
+        np.testing.assert_allclose(part[0][b, h, i * bq:(i + 1) * bq], full[0][b, h, i * bq:(i + 1) * bq], atol=1e-13)
+    for (b, h, j) in ks:
+        for t in (1, 2):
+            np.testing.assert_allclose(part[t][b, h, j * bk:(j + 1) * bk], full[t][b, h, j * bk:(j + 1) * bk],
+                                       atol=1e-13)
+    assert np.isnan(part[0][0, 0, 0]).all() and np.isnan(part[1][0, 0, 0]).all()
+
+
+def test_error_scales_bound_the_gradients():
+    """|x . y| <= |x| . |y| termwise: each scale is at least the magnitude of its gradient."""
+    n, d, bq, bk = 96, 8, 32, 16
+    q, k, v, g = _inputs(1, 2, n, d, 31)
+    rng = np.random.default_rng(32)
+    mask = (rng.random((1, 2, 3, 6)) < 0.6).astype(np.uint8)
+    grads = bw.masked_attention_bwd(q, k, v, mask, g, bq, bk)
+    scales = bw.masked_attention_bwd_scales(q, k, v, mask, g, bq, bk)
+    for a, s in zip(grads, scales):
+        assert (np.abs(a) <= s + 1e-12).all()
+    part = bw.masked_attention_bwd_scales(q, k, v, mask, g, bq, bk, q_blocks=[(0, 1, 1)], k_blocks=[(0, 0, 2)])
+    np.testing.assert_allclose(part[0][0, 1, 32:64], scales[0][0, 1, 32:64], atol=1e-13)
+    np.testing.assert_allclose(part[1][0, 0, 32:48], scales[1][0, 0, 32:48], atol=1e-13)
