@@ -27,7 +27,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan720p_traffic.json")
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_query_amd", "csrc", f)
-                for f in ("attn_fwd.hip", "sa_common.h")]
+                for f in ("attn_fwd.hip", "attn_tiles.h", "sa_common.h")]
 
 
 def attn_source_digest() -> str:
@@ -196,6 +196,52 @@ def pattern_bench(args, sa, w, q, k, v, gen_s):
     }
 
 
+def backward_bench(args, sa, w, q, k, v, gen_s):
+    """sparse_attn_bwd on the hybrid mask of the workload. Algorithmic FLOPs are 2.5x the forward's
+    executed FLOPs (S, dP, dV, dQ, dK at 2 d per kept (query, key) pair); the kernels recompute S
+    and dP once more for dQ, which is not credited."""
+    import torch
+    B, H, N, d = q.shape
+    qp, kp = sa.pool_qk(q, k, w.bq, w.bk)
+    sel = sa.select_mask(qp, kp, w.k_frac, w.p)
+    o, lse = sa.fwd(q, k, v, sel["mask"], w.bq, w.bk, return_lse=True)
+    g = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(q.dtype).to(q.device)
+    ws = torch.empty(sa.bwd_workspace_size(B, H, N, w.bq, w.bk), dtype=torch.uint8, device=q.device)
+    outs = tuple(torch.empty_like(q) for _ in range(3))
+    mask_cpu = sel["mask"].cpu().numpy()
+    fwd_flops = executed_flops(mask_cpu, N, w.bq, w.bk, d)
+    flops = 2.5 * fwd_flops
+
+    def step():
+        sa.bwd(q, k, v, o, g, lse, sel["mask"], w.bq, w.bk, workspace=ws, out=outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "block-sparse attention backward TFLOP/s (algorithmic: 2.5x forward executed FLOPs)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: backward on the hybrid mask", "batch": B, "heads": H, "tokens": N,
+                   "head_dim": d, "bq": w.bq, "bk": w.bk, "k_frac": w.k_frac, "p": w.p,
+                   "kept_block_density": round(float(mask_cpu.mean()), 5),
+                   "algorithmic_tflop_per_step": round(flops / 1e12, 4), "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "sparse_attn_bwd (delta, dQ, dK/dV kernels)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "input_generation_s": round(gen_s, 1),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +258,9 @@ def main(argv=None):
                          "windows of 240 tokens, then the same-position pass in the window-transposed order). "
                          "vdit: Sparse-vDiT style union of a diagonal band, the band repeated every frame and the "
                          "first key token of every frame")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the block-sparse backward (sparse_attn_bwd) on the workload's hybrid mask instead "
+                         "of the forward path; the mask, O and LSE are computed once before the timed region")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -253,6 +302,9 @@ def main(argv=None):
     o = torch.empty_like(q)
     if args.pattern != "hybrid":
         print(json.dumps(pattern_bench(args, sa, w, q, k, v, gen_s)), flush=True)
+        return 0
+    if args.backward:
+        print(json.dumps(backward_bench(args, sa, w, q, k, v, gen_s)), flush=True)
         return 0
 
     def step(ev=None):
