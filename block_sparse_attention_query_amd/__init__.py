@@ -22,8 +22,8 @@ from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA
 
 __all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
-           "window_transpose", "squad_attention", "topk_count", "sparse_attention",
-           "SparseAttnError"]
+           "window_transpose", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
+           "probe_workspace_size", "SparseAttnError"]
 
 _DTYPES = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}
 
@@ -257,3 +257,28 @@ def bwd(q, k, v, o, dout, lse, mask, bq: int, bk: int = 64, scale: float | None 
                                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                                           workspace.numel() * workspace.element_size(), _stream(q)))
     return dq, dk, dv
+
+
+def probe_workspace_size(B: int, H: int, N: int, d: int, bq: int, probes: int) -> int:
+    return int(_lib.lib().sparse_attn_probe_workspace_size(B, H, N, d, bq, probes))
+
+
+def probe_correct(q, k, v, o, bq: int, probes: int, ridge: float, scale: float | None = None,
+                  workspace: torch.Tensor | None = None, return_fit: bool = False):
+    """Probe-fitted residual correction of the sparse output ``o`` (bf16), in place.
+
+    With ``return_fit`` also returns A (float32 ``[B, H, d + 1, d]``) and the exact probe rows
+    (float32 ``[B, H, probes * bq, d]``)."""
+    _check_qkv(q, k, v, o)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    workspace = _workspace(probe_workspace_size(B, H, N, d, bq, probes), workspace, q.device)
+    a = exact = None
+    if return_fit:
+        a = torch.empty((B, H, d + 1, d), dtype=torch.float32, device=q.device)
+        exact = torch.empty((B, H, probes * bq, d), dtype=torch.float32, device=q.device)
+    _lib.check(_lib.lib().sparse_attn_probe_correct(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _DTYPES[q.dtype], B, H, N, d, bq, scale, int(probes),
+        float(ridge), a.data_ptr() if a is not None else None, exact.data_ptr() if exact is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
+    return (o, a, exact) if return_fit else o

@@ -28,6 +28,10 @@ hipError_t launch_pattern_mask(int kinds, int window, int band, int period, int 
                                uint8_t* mask, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
 hipError_t launch_window_transpose(const void* x, void* out, int BH, int N, int row_bytes, int w, int inverse,
                                    hipStream_t stream);
+size_t probe_workspace_bytes(int BH, int N, int d, int Bq, int P);
+hipError_t launch_probe(const void* q, const void* k, const void* v, void* o, int BH, int N, int d, int Bq,
+                        double scale, int P, double ridge, float* a_user, float* exact_user, void* ws,
+                        hipStream_t stream);
 }  // namespace sa
 
 namespace {
@@ -215,6 +219,38 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   return hip_status(sa::launch_bwd(q, k, v, o, dout, lse, mask, B * H, N, d, Bq, scale, dq, dk, dv, workspace,
                                    static_cast<hipStream_t>(stream)),
                     "bwd launch");
+}
+
+size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int probes) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128) || (Bq != 64 && Bq != 128) || probes < 1 || probes > 1024)
+    return 0;
+  if ((long long)B * H > 65535) return 0;
+  return sa::probe_workspace_bytes(B * H, N, d, Bq, probes);
+}
+
+int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void* o, int dtype, int B, int H, int N,
+                              int d, int Bq, double scale, int probes, double ridge, float* a_out, float* exact_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(SA_ERR_INVALID_ARG, "probe_correct: null workspace");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "probe_correct: only SA_BF16 tensors are supported");
+  if (probes < 1 || probes > 1024) return fail(SA_ERR_INVALID_ARG, "probe_correct: probes=%d not in [1, 1024]", probes);
+  if (!(ridge > 0.0) || !isfinite(ridge)) return fail(SA_ERR_INVALID_ARG, "probe_correct: ridge must be finite and > 0");
+  if ((reinterpret_cast<uintptr_t>(a_out) & 15u) || (reinterpret_cast<uintptr_t>(exact_out) & 15u))
+    return fail(SA_ERR_INVALID_ARG, "probe_correct: a_out and exact_out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(SA_ERR_INVALID_ARG, "probe_correct: workspace must be 256-byte aligned");
+  const size_t need = sparse_attn_probe_workspace_size(B, H, N, d, Bq, probes);
+  if (need == 0) return fail(SA_ERR_UNSUPPORTED, "probe_correct: unsupported sizes");
+  if (workspace_bytes < need)
+    return fail(SA_ERR_INVALID_ARG, "probe_correct: workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, need);
+  if ((long long)B * H * probes * cdiv(N, 64) > 0x7fffffffLL || (long long)B * H * cdiv(N, 256) > 0x7fffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "probe_correct: too many workgroups");
+  return hip_status(sa::launch_probe(q, k, v, o, B * H, N, d, Bq, scale, probes, ridge, a_out, exact_out, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                    "probe_correct launch");
 }
 
 int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int B, int H, int N, int Bq, int Bk,

@@ -203,6 +203,40 @@ int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int
 int sparse_attn_window_transpose(const void* x, int dtype, int B, int H, int N, int d, int window, int inverse,
                                  void* out, void* stream);
 
+/*
+ * Bytes of device scratch sparse_attn_probe_correct needs (0 if the sizes are invalid).
+ */
+size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int probes);
+
+/*
+ * Probe-fitted residual correction of a sparse output, in place ([SPR] original abstract: a few
+ * exact query rows calibrate an affine correction from the sparse output, within the output
+ * subspace of the probe residuals). Per (b, h):
+ *   probes    `probes` query blocks i_p = min(F - 1, floor((p + 1/2) F / probes)), p = 0..probes-1,
+ *             F = the number of full query blocks (nQB, or nQB - 1 when N % Bq != 0; at least 1);
+ *   exact     dense softmax attention of the probe rows over all N keys (bf16 operands, fp32
+ *             accumulation, P rounded to bf16 for the PV product, as in the forward);
+ *   fit       X = [O, 1] and R = O_exact - O on the probe rows inside the sequence (duplicated
+ *             probes count once per occurrence); A = (X^T X + mu I)^-1 X^T R in float64 by
+ *             Cholesky, mu = ridge * trace(X^T X) / (d + 1);
+ *   apply     O <- O + O A[0:d] + A[d] on every row (bf16 MFMA with A rounded to bf16, fp32
+ *             accumulation and add, result rounded to bf16).
+ *   q, k, v     device, [B, H, N, d] SA_BF16 (`dtype` must be SA_BF16).
+ *   o           device in/out, [B, H, N, d] bf16: the sparse output (e.g. of sparse_attn_fwd), replaced
+ *               by the corrected output.
+ *   probes      1 .. 1024; ridge > 0 (then X^T X + mu I is positive definite).
+ *   a_out       device out or NULL, [B, H, d + 1, d] float32: A.
+ *   exact_out   device out or NULL, [B, H, probes * Bq, d] float32: the exact probe rows in probe
+ *               order (rows past N, possible only when the sequence has no full block, are
+ *               unspecified).
+ *   workspace   device scratch of at least sparse_attn_probe_workspace_size() bytes, 256-byte
+ *               aligned; overwritten.
+ * d in {64, 128}, Bq in {64, 128}; key blocks of 64. Deterministic (no atomics).
+ */
+int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void* o, int dtype, int B, int H, int N,
+                              int d, int Bq, double scale, int probes, double ridge, float* a_out, float* exact_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host helper: the Top-k size for a fraction, as select_mask computes it (-1 if invalid). */
 int sparse_attn_topk_count(double k_frac, int nkb);
 

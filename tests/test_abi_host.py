@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -191,3 +191,37 @@ def test_bwd_workspace_size():
         al(bh * nkb * nqb) + al(bh * n * 4)
     assert lib.sparse_attn_bwd_workspace_size(1, 2, n, bq, 64) == want
     assert lib.sparse_attn_bwd_workspace_size(1, 2, n, 96, 64) == 0
+
+
+def _probe(**kw):
+    ws = _lib.lib().sparse_attn_probe_workspace_size(1, 2, 1024, 64, 64, 2)
+    a = dict(q=P, k=P, v=P, o=P, dtype=0, B=1, H=2, N=1024, d=64, Bq=64, scale=0.125, probes=2, ridge=1e-3,
+             a_out=None, exact_out=None, ws=P, ws_bytes=ws, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_probe_correct(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), -1), (dict(q=None), -1), (dict(ws=None), -1), (dict(ws_bytes=64), -1), (dict(ws=P + 16), -1),
+    (dict(o=P_ODD), -1), (dict(a_out=P_ODD), -1), (dict(exact_out=P_ODD), -1), (dict(probes=0), -1),
+    (dict(probes=1025), -1), (dict(ridge=0.0), -1), (dict(ridge=float("nan")), -1), (dict(scale=-1.0), -1),
+    (dict(dtype=1), -2), (dict(d=96), -2), (dict(Bq=32), -2), (dict(N=0), -1),
+])
+def test_probe_correct_rejects(kw, code):
+    assert _probe(**kw) == code
+
+
+def test_probe_workspace_size():
+    """Partial outputs of S key-block ranges (about 1024 workgroups in all, at least 4 key blocks
+    per range), the exact probe rows, [G | C] in float64, A, A^T in bf16 and the bias row."""
+    lib = _lib.lib()
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    bh, n, d, bq, probes = 2, 1000, 128, 128, 3
+    nkb = 16
+    s = max(1, min(-(-1024 // (bh * probes)), nkb // 4))
+    units = bh * probes * s
+    want = al(units * bq * d * 4) + al(units * bq * 8) + al(bh * probes * bq * d * 4) + \
+        al(bh * (d + 1) * (2 * d + 1) * 8) + al(bh * (d + 1) * d * 4) + al(bh * d * d * 2) + al(bh * d * 4)
+    assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, probes) == want
+    assert lib.sparse_attn_probe_workspace_size(1, 2, n, 96, bq, probes) == 0
+    assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, 0) == 0
