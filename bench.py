@@ -242,6 +242,93 @@ def backward_bench(args, sa, w, q, k, v, gen_s):
     }
 
 
+def corrected_bench(args, sa, w, q, k, v, gen_s):
+    """The hot path followed by the probe-fitted residual correction (sparse_attn_probe_correct,
+    ``--correct`` probes, ridge 1e-3). Executed FLOPs add the probes' dense attention (4 d per
+    valid probe query x key) and the applied map (2 d^2 per token) to the sparse attention's. Also
+    reports how far the sparse and the corrected outputs are from exact attention on 8 held-out
+    query blocks per head (relative L2 error), exact rows from sparse_attn_fwd with those rows'
+    masks full."""
+    import numpy as np
+    import torch
+    B, H, N, d = q.shape
+    nqb, nkb = -(-N // w.bq), -(-N // w.bk)
+    P, ridge = args.correct, 1e-3
+    qp, kp = sa.pool_qk(q, k, w.bq, w.bk)
+    sel = sa.select_mask(qp, kp, w.k_frac, w.p, kept_lists=True)
+    o = torch.empty_like(q)
+    ws = torch.empty(sa.probe_workspace_size(B, H, N, d, w.bq, P), dtype=torch.uint8, device=q.device)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sa.pool_qk(q, k, w.bq, w.bk, out=(qp, kp))
+        sa.select_mask(qp, kp, w.k_frac, w.p, kept_lists=True, out=sel)
+        if ev is not None:
+            ev[1].record()
+        sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, out=o)
+        if ev is not None:
+            ev[2].record()
+        sa.probe_correct(q, k, v, o, w.bq, P, ridge, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mask_cpu = sel["mask"].cpu().numpy()
+    full = nqb if N % w.bq == 0 else max(nqb - 1, 1)
+    probe_rows = sum(min(w.bq, N - (min(full - 1, int((p + 0.5) * full / P))) * w.bq) for p in range(P))
+    probe_flops = 4.0 * d * B * H * probe_rows * N
+    apply_flops = 2.0 * d * d * B * H * N
+    flops = executed_flops(mask_cpu, N, w.bq, w.bk, d) + probe_flops + apply_flops
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(args.steps):
+        step(evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    mask_ms, attn_ms, corr_ms = (float(x) for x in per.mean(axis=0))
+
+    # held-out quality: exact rows of 8 query blocks per head that are not probes
+    held = sorted({min(full - 1, int((j + 0.25) * full / 8)) for j in range(8)} -
+                  {min(full - 1, int((p + 0.5) * full / P)) for p in range(P)})
+    m_ex = torch.zeros((B, H, nqb, nkb), dtype=torch.uint8, device=q.device)
+    m_ex[:, :, held] = 1
+    o_ex = sa.fwd(q, k, v, m_ex, w.bq, w.bk)
+    o_s = sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk)
+    rows = torch.cat([torch.arange(i * w.bq, min(N, (i + 1) * w.bq)) for i in held]).to(q.device)
+    ex, sp, co = (t[:, :, rows].float() for t in (o_ex, o_s, o))
+    rel = lambda t: float((t - ex).norm() / ex.norm())  # noqa: E731
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "sparse attention fwd + probe-fitted correction TFLOP/s (executed)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: hybrid mask, then {P} probe blocks per head", "batch": B, "heads": H,
+                   "tokens": N, "head_dim": d, "bq": w.bq, "bk": w.bk, "k_frac": w.k_frac, "p": w.p,
+                   "probes": P, "ridge": ridge, "kept_block_density": round(float(mask_cpu.mean()), 5),
+                   "executed_tflop_per_step": round(flops / 1e12, 4),
+                   "probe_dense_tflop": round(probe_flops / 1e12, 4), "apply_tflop": round(apply_flops / 1e12, 4),
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_call": {"pool_qk+select_mask": round(mask_ms, 4), "fwd_lists": round(attn_ms, 4),
+                        "probe_correct": round(corr_ms, 4)},
+        "heldout_rel_l2_error": {"query_blocks_per_head": len(held), "sparse": round(rel(sp), 5),
+                                 "corrected": round(rel(co), 5)},
+        "roofline": {"kernel": "attn_fwd_kernel<bf16, 128, 128>", "bound": "mfma",
+                     "achieved": round(executed_flops(mask_cpu, N, w.bq, w.bk, d) / (attn_ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(executed_flops(mask_cpu, N, w.bq, w.bk, d) / (attn_ms * 1e-3) / 1e12
+                                   / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "input_generation_s": round(gen_s, 1),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +348,9 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true",
                     help="time the block-sparse backward (sparse_attn_bwd) on the workload's hybrid mask instead "
                          "of the forward path; the mask, O and LSE are computed once before the timed region")
+    ap.add_argument("--correct", type=int, default=0, metavar="PROBES",
+                    help="time the hot path followed by the probe-fitted residual correction with PROBES probe "
+                         "query blocks per head (ridge 1e-3), and report held-out error before and after")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -305,6 +395,9 @@ def main(argv=None):
         return 0
     if args.backward:
         print(json.dumps(backward_bench(args, sa, w, q, k, v, gen_s)), flush=True)
+        return 0
+    if args.correct:
+        print(json.dumps(corrected_bench(args, sa, w, q, k, v, gen_s)), flush=True)
         return 0
 
     def step(ev=None):

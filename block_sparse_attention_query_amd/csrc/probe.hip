@@ -11,8 +11,8 @@
 //      (float64);
 //   4. A = (G + mu I)^-1 C with mu = ridge * trace(G) / (d + 1), by Cholesky factorisation;
 //   5. O <- O + [O, 1] A on every row, in place.
-// Kernels: probe_partial (MFMA, the forward's tile layout), probe_combine, probe_gram (fp64),
-// probe_solve (fp64, one workgroup per head) and probe_apply (bf16 MFMA, HBM-bound).
+// Kernels: probe_partial (MFMA, the forward's tile layout), probe_combine, probe_gram (fp64 MFMA),
+// probe_chol and probe_subst (fp64) and probe_apply (bf16 MFMA, HBM-bound).
 #include <algorithm>
 
 #include "attn_tiles.h"
@@ -239,168 +239,384 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 
 // ---------------------------------------------------------------- 3. [G | C] = X^T [X | R]
 
-// Grid (BH, ceil((D + 1) / 32)): rows i0 .. i0 + 31 of the (D + 1) x (2 D + 1) matrix [G | C],
-// summed in float64 over the probe rows that lie inside the sequence. X = [O_sparse, 1] from the
-// bf16 output, R = O_exact - O_sparse.
+// Z = [X | R] on the probe rows, X = [O_sparse, 1] (bf16 output widened to float64, rows past
+// the sequence zero) and R = O_exact - O_sparse; [G | C] = X^T Z is a (D + 1) x (2 D + 1) float64
+// product over the m = P BQ probe rows, on the matrix cores (v_mfma_f64_16x16x4f64: lane j holds
+// A[j % 16][j / 16] and B[j / 16][j % 16] of a 16x4 / 4x16 step; element i of the result is
+// C[4 i + j / 16][j % 16]). Grid (BH, ceil((D + 1) / 16)): a workgroup of 4 waves computes the
+// 16 rows i0 .. i0 + 15 of [G | C] (A = Z[:, i0 .. i0 + 15]^T), its waves splitting the 16-column
+// tiles; Z is staged through LDS 16 probe rows at a time, the next stage prefetched in registers.
+template <int D>
+struct GramCfg {
+  static constexpr int n = D + 1, W = 2 * D + 1;
+  static constexpr int NJ = (W + 15) / 16;        // 16-column tiles of [G | C]
+  static constexpr int ZW = NJ * 16;              // staged columns (zero past W)
+  static constexpr int ZS = ZW + 2;               // LDS row stride (doubles)
+  static constexpr int CH = 16;                   // probe rows per stage
+  static constexpr int EPT = (CH * ZW + 255) / 256;
+  static constexpr int TPW = (NJ + 3) / 4;        // column tiles per wave
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void probe_gram_kernel(const uint16_t* __restrict__ o, const float* __restrict__ exact,
                                                          int N, int nqb, int BQ, int P, double* __restrict__ gram) {
-  constexpr int W = 2 * D + 1;      // columns of [G | C]
-  constexpr int CH = 16;            // probe rows per LDS stage
-  constexpr int JPT = (W + 7) / 8;  // columns per thread
-  __shared__ double z[CH][W + 1];   // [X | R] of CH probe rows
-  const int bh = blockIdx.x;
-  const int i = blockIdx.y * 32 + (threadIdx.x & 31);
-  const int jg = threadIdx.x >> 5;  // this thread's columns: jg, jg + 8, ...
-  double acc[JPT];
-#pragma unroll
-  for (int t = 0; t < JPT; ++t) acc[t] = 0.0;
+  using G = GramCfg<D>;
+  constexpr int n = G::n, W = G::W, NJ = G::NJ, ZW = G::ZW, ZS = G::ZS, CH = G::CH, EPT = G::EPT, TPW = G::TPW;
+  __shared__ double z[CH * ZS];
+  __shared__ int ptok[1024];  // first token of each probe block
+  const int bh = blockIdx.x, i0 = blockIdx.y * 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int p = tid; p < P; p += 256) ptok[p] = probe_block(p, P, nqb, N, BQ) * BQ;
+  __syncthreads();
+  const uint16_t* oh = o + (size_t)bh * N * D;
+  const float* eh = exact + (size_t)bh * P * BQ * D;
   const int m = P * BQ;
+  // Z[pr][col] for the stage: both loads of every element are issued unconditionally (clamped
+  // addresses) so that they overlap, and the element is selected afterwards.
+  double pre[EPT];
+  auto fetch = [&](int r0) {
+    uint16_t ov[EPT];
+    float ev[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = tid + 256 * u;
+      const int pr = min(r0 + e / ZW, m - 1), col = e % ZW;
+      const int p = pr / BQ, qq = pr - p * BQ;
+      const int tok = min(ptok[p] + qq, N - 1);
+      const int ch = col < D ? col : (col >= n && col < W ? col - n : 0);
+      ov[u] = oh[(size_t)tok * D + ch];
+      ev[u] = eh[((size_t)p * BQ + qq) * D + ch];
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = tid + 256 * u;
+      const int pr = r0 + e / ZW, col = e % ZW;
+      const int p = min(pr, m - 1) / BQ;
+      const bool valid = e < CH * ZW && pr < m && ptok[p] + (min(pr, m - 1) - p * BQ) < N;
+      const double x = (double)__uint_as_float((uint32_t)ov[u] << 16);
+      const double z = col < D ? x : (col == D ? 1.0 : (col < W ? (double)ev[u] - x : 0.0));
+      pre[u] = valid ? z : 0.0;
+    }
+  };
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  f64x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int jr = lane & 15, jk = lane >> 4;
+  fetch(0);
   for (int r0 = 0; r0 < m; r0 += CH) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < CH * (D + 1); e += 256) {
-      const int rr = e / (D + 1), c = e % (D + 1);
-      const int pr = r0 + rr;
-      const int p = pr / BQ, qq = pr % BQ;
-      double xs = 0.0, xe = 0.0;
-      if (pr < m) {
-        const int tok = probe_block(p, P, nqb, N, BQ) * BQ + qq;
-        if (tok < N) {
-          if (c < D) {
-            xs = (double)__uint_as_float((uint32_t)o[((size_t)bh * N + tok) * D + c] << 16);
-            xe = (double)exact[(((size_t)bh * P + p) * BQ + qq) * D + c];
-          } else {
-            xs = 1.0;
-          }
-        }
-      }
-      z[rr][c] = xs;
-      if (c < D) z[rr][D + 1 + c] = xe - xs;
+    __syncthreads();  // the previous stage has been consumed
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = tid + 256 * u;
+      if (e < CH * ZW) z[(e / ZW) * ZS + e % ZW] = pre[u];
     }
     __syncthreads();
-    if (i <= D) {
-#pragma unroll 1
-      for (int rr = 0; rr < CH; ++rr) {
-        const double xi = z[rr][i];
+    if (r0 + CH < m) fetch(r0 + CH);
 #pragma unroll
-        for (int t = 0; t < JPT; ++t) {
-          const int j = jg + 8 * t;
-          if (j < W) acc[t] = fma(xi, z[rr][j], acc[t]);
-        }
+    for (int s = 0; s < CH / 4; ++s) {
+      const double a = z[(4 * s + jk) * ZS + i0 + jr];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int jt = wave + 4 * t;
+        if (jt < NJ)
+          acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, z[(4 * s + jk) * ZS + 16 * jt + jr], acc[t], 0, 0, 0);
       }
     }
   }
-  if (i <= D) {
 #pragma unroll
-    for (int t = 0; t < JPT; ++t) {
-      const int j = jg + 8 * t;
-      if (j < W) gram[((size_t)bh * (D + 1) + i) * W + j] = acc[t];
+  for (int t = 0; t < TPW; ++t) {
+    const int jt = wave + 4 * t;
+    const int col = 16 * jt + jr;
+    if (jt < NJ && col < W) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i0 + 4 * i + jk;
+        if (row < n) gram[((size_t)bh * n + row) * W + col] = acc[t][i];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- 4. ridge solve
 
-// One workgroup (4 waves) per head, float64. The lower triangle of G + mu I is factorised in
-// packed storage (row r at offset r (r + 1) / 2; the pivots are kept apart) by right-looking
-// Cholesky steps, then the D right-hand sides C are solved 64 columns at a time (lane = column)
-// by blocked forward and back substitution: 32-row blocks, whose updates from the solved rows use
-// all four waves and whose diagonal triangles use one. Writes A (fp32 [D + 1][D]), A[0:D]^T as
-// bf16 [D][D] (the apply kernel's operand) and the bias row A[D] (fp32).
+// Two kernels, float64 throughout.
+//
+// probe_chol: one workgroup of 1024 threads per head factorises G + mu I = L L^T by right-looking
+// Cholesky steps on the unscaled trailing matrix (M' = M - m_k m_k^T / m_kk over the rows and
+// columns past k, L[:, k] = m_k / sqrt(m_kk)). Every element of the lower triangle stays in the
+// register of the thread that owns it (column-major packed index E, owner E mod 1024, so that a
+// wave's slot covers one or two columns and drops out as a whole once the factorisation has
+// passed them); step k only publishes column k through LDS (double-buffered, one barrier per
+// step). The factor is written out as a square array whose rows are padded to whole row blocks,
+// L below the diagonal, L^T above it and zeros in the padding, so that both substitutions read
+// contiguous row segments, followed by the n reciprocals 1 / L[r][r].
+//
+// probe_subst: grid (heads, D / 32), 256 threads; each workgroup copies the factor to LDS and
+// solves 32 of the D right-hand-side columns, which stay in registers: thread (c, rs) holds rows
+// rs + 8 u of column c. Forward (L Y = C) and back (L^T A = Y) substitution run over blocks of 8
+// rows: the block's values of each column go through LDS once, every thread finishes the whole
+// block for its column (a small triangle, computed redundantly instead of a second barrier),
+// then updates its own later (earlier) rows. Writes A (fp32 [D + 1][D]), A[0:D]^T as bf16 [D][D]
+// (the apply kernel's operand) and the bias row A[D] (fp32).
 template <int D>
-__global__ __launch_bounds__(256) void probe_solve_kernel(const double* __restrict__ gram, double ridge,
-                                                          float* __restrict__ a_out, __bf16* __restrict__ at_out,
-                                                          float* __restrict__ bias_out) {
-  constexpr int n = D + 1, W = 2 * D + 1, G = 64, YS = G + 1, RB = 32;
+struct SolveCfg {
+  static constexpr int n = D + 1, W = 2 * D + 1;
+  static constexpr int NT = 1024;                      // factorisation threads
+  static constexpr int CW = 32;                        // right-hand-side columns per workgroup
+  static constexpr int ST = 256;                       // substitution threads
+  static constexpr int RS = ST / CW;                   // row sets (= rows per block)
+  static constexpr int RPER = (n + RS - 1) / RS;       // rows per thread (= row blocks)
+  static constexpr int SS = RPER * RS;                 // padded row stride of the factor (doubles)
+  static constexpr int FAC = (n * SS + n + 1) & ~1;   // factor + reciprocals, doubles per head (even)
+  static constexpr int TRI = n * (n + 1) / 2;          // lower triangle
+  static constexpr int EPT = (TRI + NT - 1) / NT;      // factor elements per thread
+  static constexpr int TS = D + 8;                     // bf16 row stride of the transposed copy
+  static constexpr size_t CHOL_LDS = (size_t)n * SS * 8 + 2 * n * 8 + n * 8;
+  static constexpr size_t SUBST_LDS = (size_t)FAC * 8 + 2 * RS * CW * 8;
+  static_assert(D % CW == 0, "column groups");
+  static_assert((size_t)CW * TS * 2 <= (size_t)n * SS * 8, "transposed copy must fit in the factor's space");
+  static_assert(CHOL_LDS <= 160 * 1024 - 1024 && SUBST_LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+__global__ __launch_bounds__(1024) void probe_chol_kernel(const double* __restrict__ gram, double ridge,
+                                                          double* __restrict__ fac) {
+  using S = SolveCfg<D>;
+  constexpr int n = S::n, W = S::W, NT = S::NT, SS = S::SS, TRI = S::TRI, EPT = S::EPT;
   extern __shared__ __attribute__((aligned(16))) double sm[];
-  double* L = sm;                    // n (n + 1) / 2, packed lower triangle
-  double* Y = sm + n * (n + 1) / 2;  // n x YS, right-hand sides / solution columns
-  __shared__ double piv[n];
-  __shared__ double red[256];
-  const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  double* Lf = sm;               // n x SS: L (lower), L^T (upper), zero padding
+  double* col = Lf + n * SS;     // 2 x n: column k of the trailing matrix
+  double* invd = col + 2 * n;    // n: 1 / L[r][r]
+  __shared__ double red[NT / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double* g = gram + (size_t)bh * n * W;
-  auto at = [](int r, int c) { return r * (r + 1) / 2 + c; };
 
-  for (int r = wave; r < n; r += 4)
-    for (int c = lane; c <= r; c += 64) L[at(r, c)] = g[(size_t)r * W + c];
+  for (int e = tid; e < n * SS; e += NT) Lf[e] = 0.0;
   double tr = 0.0;
-  for (int r = tid; r < n; r += 256) tr += g[(size_t)r * W + r];
-  red[tid] = tr;
+  for (int r = tid; r < n; r += NT) tr += g[(size_t)r * W + r];
+  for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o, 64);
+  if (lane == 0) red[wave] = tr;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
+  tr = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) tr += red[w];
+  const double mu = ridge * tr / n;
+
+  // owned elements of the lower triangle, column-major: column c starts at c n - c (c - 1) / 2
+  // (ec = -1: none)
+  int er[EPT], ec[EPT];
+  double m[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + NT * j;
+    er[j] = 0;
+    ec[j] = -1;
+    m[j] = 0.0;
+    if (e < TRI) {
+      auto start = [](int c) { return c * n - c * (c - 1) / 2; };
+      const float b2 = 2.f * n + 1.f;
+      int c = (int)((b2 - sqrtf(b2 * b2 - 8.f * (float)e)) * 0.5f);
+      c = c < 0 ? 0 : (c > n - 1 ? n - 1 : c);
+      while (c > 0 && start(c) > e) --c;
+      while (c < n - 1 && start(c + 1) <= e) ++c;
+      const int r = c + e - start(c);
+      er[j] = r;
+      ec[j] = c;
+      m[j] = g[(size_t)r * W + c] + (r == c ? mu : 0.0);
+    }
   }
-  const double mu = ridge * red[0] / n;
-  for (int r = tid; r < n; r += 256) L[at(r, r)] += mu;
+  for (int k = 0; k < n; ++k) {
+    double* cb = col + (k & 1) * n;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (ec[j] == k) cb[er[j]] = m[j];  // column k after step k - 1
+    __syncthreads();
+    const double dk = cb[k];  // > 0: G + mu I is positive definite for mu > 0
+    // 1 / sqrt(dk): the hardware estimate and one Newton step
+    double rsq = __builtin_amdgcn_rsq(dk);
+    rsq = rsq * fma(-0.5 * dk * rsq, rsq, 1.5);
+    const double inv = rsq * rsq;
+    // slots of finished columns are skipped (wave-uniform); the live slots' loads are all issued
+    // before the first use
+    bool act[EPT];
+    double va[EPT], vb[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      act[j] = __ballot(ec[j] >= k) != 0;
+      va[j] = 0.0;
+      vb[j] = 0.0;
+      if (act[j]) {
+        va[j] = cb[er[j]];
+        vb[j] = cb[ec[j] < 0 ? 0 : ec[j]];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      if (act[j]) {
+        const double upd = fma(-va[j] * inv, vb[j], m[j]);
+        m[j] = ec[j] > k ? upd : (ec[j] == k ? m[j] * rsq : m[j]);
+      }
+    }
+  }
+  __syncthreads();  // the zero fill is complete
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (ec[j] >= 0) {
+      Lf[er[j] * SS + ec[j]] = m[j];
+      Lf[ec[j] * SS + er[j]] = m[j];
+      if (er[j] == ec[j]) invd[er[j]] = 1.0 / m[j];
+    }
+  }
   __syncthreads();
+  double* fo = fac + (size_t)bh * S::FAC;
+  for (int e = tid; e < n * SS; e += NT) fo[e] = Lf[e];
+  for (int e = tid; e < n; e += NT) fo[n * SS + e] = invd[e];
+}
 
-  for (int kk = 0; kk < n; ++kk) {
-    const double pk = sqrt(L[at(kk, kk)]);  // > 0: G + mu I is positive definite for mu > 0
-    if (tid == 0) piv[kk] = pk;
-    const double inv = 1.0 / pk;
-    for (int r = kk + 1 + tid; r < n; r += 256) L[at(r, kk)] *= inv;
-    __syncthreads();
-    for (int r = kk + 1 + wave; r < n; r += 4) {
-      const double lr = L[at(r, kk)];
-      for (int c = kk + 1 + lane; c <= r; c += 64) L[at(r, c)] -= lr * L[at(c, kk)];
-    }
-    __syncthreads();
+template <int D>
+__global__ __launch_bounds__(256) void probe_subst_kernel(const double* __restrict__ gram,
+                                                          const double* __restrict__ fac, float* __restrict__ a_out,
+                                                          __bf16* __restrict__ at_out, float* __restrict__ bias_out) {
+  using S = SolveCfg<D>;
+  constexpr int n = S::n, W = S::W, CW = S::CW, RS = S::RS, RPER = S::RPER, SS = S::SS;
+  extern __shared__ __attribute__((aligned(16))) double sm[];
+  double* Lf = sm;               // n x SS
+  double* invd = Lf + n * SS;    // n
+  double* ytmp = sm + S::FAC;    // 2 x RS x CW: one row block of the right-hand sides
+  const int bh = blockIdx.x, c0 = blockIdx.y * CW, tid = threadIdx.x;
+  const double* g = gram + (size_t)bh * n * W;
+  {
+    const double2* src = reinterpret_cast<const double2*>(fac + (size_t)bh * S::FAC);
+    double2* dst = reinterpret_cast<double2*>(sm);
+    for (int e = tid; e < S::FAC / 2; e += S::ST) dst[e] = src[e];
   }
-
-  for (int c0 = 0; c0 < D; c0 += G) {
-    for (int r = wave; r < n; r += 4) Y[r * YS + lane] = c0 + lane < D ? g[(size_t)r * W + n + c0 + lane] : 0.0;
+  const int c = tid % CW, rs = tid / CW;
+  double y[RPER];
+#pragma unroll
+  for (int u = 0; u < RPER; ++u) {
+    const int row = rs + RS * u;
+    y[u] = row < n ? g[(size_t)row * W + n + c0 + c] : 0.0;
+  }
+  __syncthreads();
+  // Forward substitution L Y = C. Before block K the register array is rotated left by K: y[p]
+  // holds row rs + RS (K + p) for p < RPER - K, the finished rows sit behind them, and after the
+  // last block every row is back at y[u].
+  for (int K = 0; K < RPER; ++K) {
+    double* yt = ytmp + (K & 1) * RS * CW;
+    if (K * RS + rs < n) yt[rs * CW + c] = y[0];
     __syncthreads();
-    // forward substitution L y = c
-    for (int r0 = 0; r0 < n; r0 += RB) {
-      const int rb = min(RB, n - r0);
-      if (r0 > 0) {
-        for (int i = wave; i < rb; i += 4) {
-          const int row = r0 + i;
-          double s = 0.0;
-          for (int j = 0; j < r0; ++j) s = fma(L[at(row, j)], Y[j * YS + lane], s);
-          Y[row * YS + lane] -= s;
-        }
-        __syncthreads();
-      }
-      if (wave == 0) {
-        for (int i = 0; i < rb; ++i) {
-          const int row = r0 + i;
-          double s = Y[row * YS + lane];
-          for (int j = r0; j < row; ++j) s -= L[at(row, j)] * Y[j * YS + lane];
-          Y[row * YS + lane] = s / piv[row];
-        }
-      }
-      __syncthreads();
+    double yv[RS], yf[RS];
+#pragma unroll
+    for (int l = 0; l < RS; ++l) yv[l] = yt[l * CW + c];
+#pragma unroll
+    for (int l = 0; l < RS; ++l) {
+      const int row = K * RS + l;
+      const int rc = row < n ? row : n - 1;
+      const double* lr = Lf + rc * SS + K * RS;
+      double s = yv[l];
+#pragma unroll
+      for (int l2 = 0; l2 < l; ++l2) s = fma(-lr[l2], yf[l2], s);
+      yf[l] = row < n ? s * invd[rc] : 0.0;
     }
-    // back substitution L^T a = y
-    for (int r1 = n; r1 > 0; r1 -= RB) {
-      const int r0 = max(0, r1 - RB);
-      if (r1 < n) {
-        for (int i = wave; i < r1 - r0; i += 4) {
-          const int row = r0 + i;
-          double s = 0.0;
-          for (int j = r1; j < n; ++j) s = fma(L[at(j, row)], Y[j * YS + lane], s);
-          Y[row * YS + lane] -= s;
+    double own = 0.0;
+#pragma unroll
+    for (int l = 0; l < RS; ++l)
+      if (l == rs) own = yf[l];
+#pragma unroll
+    for (int p0 = 1; p0 < RPER; p0 += 2) {
+      // two rows at a time: their loads overlap, and the pin below keeps the next pair's loads
+      // from being issued ahead (register pressure)
+      double s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = p0 + h, row = rs + RS * (K + p);
+        s[h] = 0.0;
+        if (p < RPER && p < RPER - K && row < n) {
+          const double* lr = Lf + row * SS + K * RS;
+          s[h] = y[p];
+#pragma unroll
+          for (int l = 0; l < RS; ++l) s[h] = fma(-lr[l], yf[l], s[h]);
         }
-        __syncthreads();
       }
-      if (wave == 0) {
-        for (int row = r1 - 1; row >= r0; --row) {
-          double s = Y[row * YS + lane];
-          for (int j = row + 1; j < r1; ++j) s -= L[at(j, row)] * Y[j * YS + lane];
-          Y[row * YS + lane] = s / piv[row];
-        }
+      asm volatile("" : "+v"(s[0]), "+v"(s[1])::"memory");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = p0 + h, row = rs + RS * (K + p);
+        if (p < RPER && p < RPER - K && row < n) y[p] = s[h];
       }
-      __syncthreads();
     }
-    if (c0 + lane < D) {
-      for (int r = wave; r < n; r += 4) a_out[((size_t)bh * n + r) * D + c0 + lane] = (float)Y[r * YS + lane];
-      if (wave == 0) bias_out[(size_t)bh * D + c0 + lane] = (float)Y[D * YS + lane];
-    }
-    for (int c = wave; c < G && c0 + c < D; c += 4)
-      for (int r = lane; r < D; r += 64) at_out[((size_t)bh * D + c0 + c) * D + r] = (__bf16)Y[r * YS + c];
+#pragma unroll
+    for (int p = 0; p + 1 < RPER; ++p) y[p] = y[p + 1];
+    y[RPER - 1] = own;
+  }
+  __syncthreads();  // the last forward block's values are read before the buffers are reused
+  // Back substitution L^T A = Y, blocks K = RPER - 1 .. 0 at steps j = RPER - 1 - K. Before step
+  // j the array is rotated right by j: y[RPER - 1] holds row rs + RS K and y[p] row rs + RS (p - j)
+  // for j <= p < RPER - 1. Row `row` of the square array holds L^T[row][col] for col > row.
+  for (int j = 0; j < RPER; ++j) {
+    const int K = RPER - 1 - j;
+    double* yt = ytmp + (j & 1) * RS * CW;
+    if (K * RS + rs < n) yt[rs * CW + c] = y[RPER - 1];
     __syncthreads();
+    double yv[RS], yf[RS];
+#pragma unroll
+    for (int l = 0; l < RS; ++l) yv[l] = yt[l * CW + c];
+#pragma unroll
+    for (int l = RS - 1; l >= 0; --l) {
+      const int row = K * RS + l;
+      const int rc = row < n ? row : n - 1;
+      const double* lr = Lf + rc * SS + K * RS;
+      double s = yv[l];
+#pragma unroll
+      for (int l2 = l + 1; l2 < RS; ++l2) s = fma(-lr[l2], yf[l2], s);
+      yf[l] = row < n ? s * invd[rc] : 0.0;
+    }
+    double own = 0.0;
+#pragma unroll
+    for (int l = 0; l < RS; ++l)
+      if (l == rs) own = yf[l];
+#pragma unroll
+    for (int p0 = 0; p0 + 1 < RPER; p0 += 2) {
+      double s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = p0 + h;
+        s[h] = 0.0;
+        if (p + 1 < RPER && p >= j) {
+          const int row = rs + RS * (p - j);  // a row of an earlier block, < n
+          const double* lr = Lf + row * SS + K * RS;
+          s[h] = y[p];
+#pragma unroll
+          for (int l = 0; l < RS; ++l) s[h] = fma(-lr[l], yf[l], s[h]);
+        }
+      }
+      asm volatile("" : "+v"(s[0]), "+v"(s[1])::"memory");
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = p0 + h;
+        if (p + 1 < RPER && p >= j) y[p] = s[h];
+      }
+    }
+#pragma unroll
+    for (int p = RPER - 1; p > 0; --p) y[p] = y[p - 1];
+    y[0] = own;
+  }
+  // outputs: A rows from registers; A^T in bf16 through a transposed LDS copy
+  __syncthreads();
+  __bf16* tl = reinterpret_cast<__bf16*>(Lf);
+#pragma unroll
+  for (int u = 0; u < RPER; ++u) {
+    const int row = rs + RS * u;
+    if (row < n) a_out[((size_t)bh * n + row) * D + c0 + c] = (float)y[u];
+    if (row < D) tl[c * S::TS + row] = (__bf16)y[u];
+    if (row == D) bias_out[(size_t)bh * D + c0 + c] = (float)y[u];
+  }
+  __syncthreads();
+  for (int e = tid; e < CW * (D / 8); e += S::ST) {
+    const int cc = e / (D / 8), ch = e % (D / 8);
+    *reinterpret_cast<uint4*>(at_out + ((size_t)bh * D + c0 + cc) * D + ch * 8) =
+        *reinterpret_cast<const uint4*>(tl + cc * S::TS + ch * 8);
   }
 }
 
@@ -484,7 +700,7 @@ namespace {
 constexpr int kApplyRows = 256;
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 struct ProbeWs {
-  size_t part_o, part_ml, exact, gram, amat, at, bias, total;
+  size_t part_o, part_ml, exact, gram, fac, amat, at, bias, total;
 };
 ProbeWs probe_ws_layout(int BH, int N, int d, int Bq, int P) {
   const int nkb = (N + BK - 1) / BK;
@@ -499,6 +715,8 @@ ProbeWs probe_ws_layout(int BH, int N, int d, int Bq, int P) {
   off += al256((size_t)BH * P * Bq * d * 4);
   w.gram = off;
   off += al256((size_t)BH * (d + 1) * (2 * d + 1) * 8);
+  w.fac = off;
+  off += al256((size_t)BH * (d == 128 ? SolveCfg<128>::FAC : SolveCfg<64>::FAC) * 8);
   w.amat = off;
   off += al256((size_t)BH * (d + 1) * d * 4);
   w.at = off;
@@ -523,6 +741,7 @@ static hipError_t launch_probe_t(const void* q, const void* k, const void* v, vo
   float* part_ml = reinterpret_cast<float*>(base + w.part_ml);
   float* exact = exact_user ? exact_user : reinterpret_cast<float*>(base + w.exact);
   double* gram = reinterpret_cast<double*>(base + w.gram);
+  double* fac = reinterpret_cast<double*>(base + w.fac);
   float* amat = a_user ? a_user : reinterpret_cast<float*>(base + w.amat);
   __bf16* at = reinterpret_cast<__bf16*>(base + w.at);
   float* bias = reinterpret_cast<float*>(base + w.bias);
@@ -537,15 +756,20 @@ static hipError_t launch_probe_t(const void* q, const void* k, const void* v, vo
   hipLaunchKernelGGL(probe_combine_kernel, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, stream, part_o,
                      part_ml, rows, P, S, BQ, D, exact);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((probe_gram_kernel<D>), dim3((unsigned)BH, (unsigned)((D + 1 + 31) / 32)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((probe_gram_kernel<D>), dim3((unsigned)BH, (unsigned)((D + 1 + 15) / 16)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(o), exact, N, nqb, BQ, P, gram);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  constexpr int n = D + 1;
-  const size_t smem = ((size_t)n * (n + 1) / 2 + (size_t)n * 65) * sizeof(double);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_solve_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  using SC = SolveCfg<D>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_chol_kernel<D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)SC::CHOL_LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((probe_solve_kernel<D>), dim3((unsigned)BH), dim3(256), smem, stream, gram, ridge, amat, at, bias);
+  hipLaunchKernelGGL((probe_chol_kernel<D>), dim3((unsigned)BH), dim3(SC::NT), SC::CHOL_LDS, stream, gram, ridge, fac);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_subst_kernel<D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)SC::SUBST_LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((probe_subst_kernel<D>), dim3((unsigned)BH, (unsigned)(D / SC::CW)), dim3(SC::ST), SC::SUBST_LDS,
+                     stream, gram, fac, amat, at, bias);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tph = (N + kApplyRows - 1) / kApplyRows;
   hipLaunchKernelGGL((probe_apply_kernel<D>), dim3((unsigned)(BH * tph)), dim3(256), 0, stream,

@@ -213,15 +213,19 @@ def test_probe_correct_rejects(kw, code):
 
 def test_probe_workspace_size():
     """Partial outputs of S key-block ranges (about 1024 workgroups in all, at least 4 key blocks
-    per range), the exact probe rows, [G | C] in float64, A, A^T in bf16 and the bias row."""
+    per range), the exact probe rows, [G | C] in float64, the factor (rows padded to blocks of 8
+    plus the n reciprocals of its diagonal, an even count of float64), A, A^T in bf16 and the bias
+    row."""
     lib = _lib.lib()
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     bh, n, d, bq, probes = 2, 1000, 128, 128, 3
     nkb = 16
     s = max(1, min(-(-1024 // (bh * probes)), nkb // 4))
     units = bh * probes * s
+    m = d + 1
+    fac = (m * (-(-m // 8) * 8) + m + 1) // 2 * 2
     want = al(units * bq * d * 4) + al(units * bq * 8) + al(bh * probes * bq * d * 4) + \
-        al(bh * (d + 1) * (2 * d + 1) * 8) + al(bh * (d + 1) * d * 4) + al(bh * d * d * 2) + al(bh * d * 4)
+        al(bh * m * (2 * d + 1) * 8) + al(bh * fac * 8) + al(bh * m * d * 4) + al(bh * d * d * 2) + al(bh * d * 4)
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, probes) == want
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, 96, bq, probes) == 0
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, 0) == 0
