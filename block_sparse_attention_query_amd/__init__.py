@@ -23,7 +23,8 @@ from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA
 __all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
            "window_transpose", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
-           "probe_workspace_size", "SparseAttnError"]
+           "probe_workspace_size", "kmeans", "cluster_select", "permute_rows", "cluster_fwd", "svg2_attention",
+           "SparseAttnError"]
 
 _DTYPES = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}
 
@@ -282,3 +283,88 @@ def probe_correct(q, k, v, o, bq: int, probes: int, ridge: float, scale: float |
         float(ridge), a.data_ptr() if a is not None else None, exact.data_ptr() if exact is not None else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, a, exact) if return_fit else o
+
+
+def kmeans(x, C: int, iters: int, init: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Lloyd's k-means of the token rows of ``x`` (bf16 ``[B, H, N, d]``) into ``C`` clusters per
+    head. Returns a dict with ``centroids`` (float32 ``[B, H, C, d]``), ``labels`` and ``perm``
+    (int32 ``[B, H, N]``) and ``offsets`` (int32 ``[B, H, C + 1]``)."""
+    _check_qkv(x)
+    B, H, N, d = x.shape
+    if init is not None and (init.dtype != torch.float32 or tuple(init.shape) != (B, H, C, d)
+                             or not init.is_contiguous() or init.device != x.device):
+        raise ValueError(f"init must be a contiguous float32 [{B}, {H}, {C}, {d}] tensor on {x.device}")
+    workspace = _workspace(int(_lib.lib().sparse_attn_kmeans_workspace_size(B, H, N, d, C)), workspace, x.device)
+    out = {"centroids": torch.empty((B, H, C, d), dtype=torch.float32, device=x.device),
+           "labels": torch.empty((B, H, N), dtype=torch.int32, device=x.device),
+           "perm": torch.empty((B, H, N), dtype=torch.int32, device=x.device),
+           "offsets": torch.empty((B, H, C + 1), dtype=torch.int32, device=x.device)}
+    _lib.check(_lib.lib().sparse_attn_kmeans(
+        x.data_ptr(), _DTYPES[x.dtype], B, H, N, d, int(C), int(iters), init.data_ptr() if init is not None else None,
+        out["centroids"].data_ptr(), out["labels"].data_ptr(), out["perm"].data_ptr(), out["offsets"].data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x)))
+    return out
+
+
+def cluster_select(cq: torch.Tensor, ck: torch.Tensor, k_offsets: torch.Tensor, p: float, scale: float | None = None,
+                   return_probs: bool = False):
+    """Centroid Top-p: uint8 mask ``[B, H, Cq, Ck]`` (and the float64 masses)."""
+    B, H, Cq, d = cq.shape
+    Ck = ck.shape[2]
+    for t, dt in ((cq, torch.float32), (ck, torch.float32), (k_offsets, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous() or t.device != cq.device:
+            raise ValueError("cq, ck must be contiguous float32 and k_offsets contiguous int32 on one device")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    mask = torch.empty((B, H, Cq, Ck), dtype=torch.uint8, device=cq.device)
+    probs = torch.empty((B, H, Cq, Ck), dtype=torch.float64, device=cq.device) if return_probs else None
+    _lib.check(_lib.lib().sparse_attn_cluster_select(
+        cq.data_ptr(), ck.data_ptr(), k_offsets.data_ptr(), B, H, Cq, Ck, d, scale, float(p),
+        probs.data_ptr() if probs is not None else None, mask.data_ptr(), _stream(cq)))
+    return (mask, probs) if return_probs else mask
+
+
+def permute_rows(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, out: torch.Tensor | None = None):
+    """Gather ``x[..., perm[t'], :]`` into row t' (or scatter row t' to ``perm[t']`` if inverse)."""
+    _check_qkv(x)
+    B, H, N, d = x.shape
+    if perm.dtype != torch.int32 or tuple(perm.shape) != (B, H, N) or not perm.is_contiguous():
+        raise ValueError(f"perm must be a contiguous int32 [{B}, {H}, {N}] tensor")
+    o = torch.empty_like(x) if out is None else _check_out(out, x.shape, x.dtype, x.device)
+    _lib.check(_lib.lib().sparse_attn_permute_rows(x.data_ptr(), _DTYPES[x.dtype], B, H, N, d, perm.data_ptr(),
+                                                   1 if inverse else 0, o.data_ptr(), _stream(x)))
+    return o
+
+
+def cluster_fwd(q, k, v, q_offsets, k_offsets, mask, bq: int = 128, scale: float | None = None,
+                return_lse: bool = False, workspace: torch.Tensor | None = None, out=None):
+    """Attention over the variable-size blocks of permuted Q / K / V (output in the query order)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    Cq, Ck = q_offsets.shape[-1] - 1, k_offsets.shape[-1] - 1
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (B, H, Cq, Ck) or not mask.is_contiguous():
+        raise ValueError(f"mask must be a contiguous uint8 [{B}, {H}, {Cq}, {Ck}] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    workspace = _workspace(int(_lib.lib().sparse_attn_cluster_fwd_workspace_size(B, H, N, Cq, Ck, bq)), workspace,
+                           q.device)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.check(_lib.lib().sparse_attn_cluster_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], B, H, N, d, q_offsets.data_ptr(), Cq,
+        k_offsets.data_ptr(), Ck, mask.data_ptr(), bq, scale, o.data_ptr(), lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def svg2_attention(q, k, v, Cq: int, Ck: int, iters: int, p: float, bq: int = 128, scale: float | None = None,
+                   init_q: torch.Tensor | None = None, init_k: torch.Tensor | None = None, return_info: bool = False):
+    """Semantic-aware permutation end to end: k-means of Q and K, centroid Top-p, attention over
+    the permuted variable-size blocks, output permuted back to the original token order."""
+    kq = kmeans(q, Cq, iters, init=init_q)
+    kk = kmeans(k, Ck, iters, init=init_k)
+    mask = cluster_select(kq["centroids"], kk["centroids"], kk["offsets"], p, scale)
+    qp, kp, vp = permute_rows(q, kq["perm"]), permute_rows(k, kk["perm"]), permute_rows(v, kk["perm"])
+    op = cluster_fwd(qp, kp, vp, kq["offsets"], kk["offsets"], mask, bq, scale)
+    o = permute_rows(op, kq["perm"], inverse=True)
+    if return_info:
+        return o, {"kmeans_q": kq, "kmeans_k": kk, "mask": mask}
+    return o

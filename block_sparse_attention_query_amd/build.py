@@ -12,10 +12,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "patterns.hip", "probe.hip"]
+SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "patterns.hip", "probe.hip", "cluster.hip"]
 # Per-source extra flags. The attention kernels assume finite-or-infinite inputs (NaN inputs give
 # unspecified outputs), which lets fmaxf on MFMA results skip the NaN-quieting canonicalize.
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_bwd.hip": ["-fno-honor-nans"], "probe.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_bwd.hip": ["-fno-honor-nans"], "probe.hip": ["-fno-honor-nans"], "cluster.hip": ["-fno-honor-nans"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.

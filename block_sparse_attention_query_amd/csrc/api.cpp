@@ -32,6 +32,18 @@ size_t probe_workspace_bytes(int BH, int N, int d, int Bq, int P);
 hipError_t launch_probe(const void* q, const void* k, const void* v, void* o, int BH, int N, int d, int Bq,
                         double scale, int P, double ridge, float* a_user, float* exact_user, void* ws,
                         hipStream_t stream);
+size_t kmeans_workspace_bytes(int BH, int N, int d, int C);
+hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, const float* init, float* cen,
+                         int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, hipStream_t stream);
+hipError_t launch_cluster_select(const float* cq, const float* ck, const int32_t* koff, int BH, int Cq, int Ck, int d,
+                                 double scale, double p, double* probs, uint8_t* mask, hipStream_t stream);
+hipError_t launch_permute_rows(const void* x, const int32_t* perm, int BH, int N, int row_bytes, int inverse,
+                               void* out, hipStream_t stream);
+int cluster_max_tiles(int N, int Cq, int Bq);
+size_t cluster_fwd_workspace_bytes(int BH, int N, int Cq, int Ck, int Bq);
+hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int BH, int N, int d, const int32_t* qoff,
+                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, int Bq, double scale, void* o,
+                              float* lse, void* ws, hipStream_t stream);
 }  // namespace sa
 
 namespace {
@@ -251,6 +263,94 @@ int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void*
   return hip_status(sa::launch_probe(q, k, v, o, B * H, N, d, Bq, scale, probes, ridge, a_out, exact_out, workspace,
                                      static_cast<hipStream_t>(stream)),
                     "probe_correct launch");
+}
+
+size_t sparse_attn_kmeans_workspace_size(int B, int H, int N, int d, int C) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128) || C <= 0 || C > SA_MAX_CLUSTERS || C > N) return 0;
+  return sa::kmeans_workspace_bytes(B * H, N, d, C);
+}
+
+int sparse_attn_kmeans(const void* x, int dtype, int B, int H, int N, int d, int C, int iters, const float* init,
+                       float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!x || !centroids || !labels || !perm || !offsets || !workspace) return fail(SA_ERR_INVALID_ARG, "kmeans: null pointer");
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "kmeans: only SA_BF16 tensors are supported");
+  if (C <= 0 || C > N) return fail(SA_ERR_INVALID_ARG, "kmeans: C=%d must lie in [1, N]", C);
+  if (C > SA_MAX_CLUSTERS) return fail(SA_ERR_UNSUPPORTED, "kmeans: C=%d exceeds %d", C, SA_MAX_CLUSTERS);
+  if (iters < 1) return fail(SA_ERR_INVALID_ARG, "kmeans: iters must be >= 1");
+  if (!aligned16(x)) return fail(SA_ERR_INVALID_ARG, "kmeans: x must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(SA_ERR_INVALID_ARG, "kmeans: workspace must be 256-byte aligned");
+  const size_t need = sparse_attn_kmeans_workspace_size(B, H, N, d, C);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_INVALID_ARG, "kmeans: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if ((long long)cdiv(N, 256) > 65535) return fail(SA_ERR_UNSUPPORTED, "kmeans: N too large");
+  return hip_status(sa::launch_kmeans(x, B * H, N, d, C, iters, init, centroids, labels, perm, offsets, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                    "kmeans launch");
+}
+
+int sparse_attn_cluster_select(const float* cq, const float* ck, const int32_t* k_offsets, int B, int H, int Cq, int Ck,
+                               int d, double scale, double p, double* probs, uint8_t* mask, void* stream) {
+  if (!cq || !ck || !k_offsets || !mask) return fail(SA_ERR_INVALID_ARG, "cluster_select: null pointer");
+  if (B <= 0 || H <= 0 || Cq <= 0 || Ck <= 0) return fail(SA_ERR_INVALID_ARG, "cluster_select: sizes must be positive");
+  if ((long long)B * H > 65535) return fail(SA_ERR_UNSUPPORTED, "cluster_select: B*H exceeds 65535");
+  if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "cluster_select: head dim %d not in {64, 128}", d);
+  if (Cq > SA_MAX_CLUSTERS || Ck > SA_MAX_CLUSTERS)
+    return fail(SA_ERR_UNSUPPORTED, "cluster_select: cluster counts exceed %d", SA_MAX_CLUSTERS);
+  if (!(scale > 0.0) || !isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "cluster_select: scale must be finite and > 0");
+  if (!(p >= 0.0 && p <= 1.0)) return fail(SA_ERR_INVALID_ARG, "cluster_select: p must lie in [0, 1]");
+  return hip_status(sa::launch_cluster_select(cq, ck, k_offsets, B * H, Cq, Ck, d, scale, p, probs, mask,
+                                              static_cast<hipStream_t>(stream)),
+                    "cluster_select launch");
+}
+
+int sparse_attn_permute_rows(const void* x, int dtype, int B, int H, int N, int d, const int32_t* perm, int inverse,
+                             void* out, void* stream) {
+  if (!x || !perm || !out) return fail(SA_ERR_INVALID_ARG, "permute_rows: null pointer");
+  int rc = check_shape(B, H, N, d);
+  if (rc) return rc;
+  if ((rc = check_dtype(dtype))) return rc;
+  if (x == out) return fail(SA_ERR_INVALID_ARG, "permute_rows: out must not alias x");
+  if (!aligned16(x) || !aligned16(out)) return fail(SA_ERR_INVALID_ARG, "permute_rows: pointers must be 16-byte aligned");
+  const long long pieces = (long long)B * H * N * (d * (dtype == SA_BF16 ? 2 : 4) / 16);
+  if ((pieces + 255) / 256 > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "permute_rows: tensor too large");
+  return hip_status(sa::launch_permute_rows(x, perm, B * H, N, d * (dtype == SA_BF16 ? 2 : 4), inverse != 0, out,
+                                            static_cast<hipStream_t>(stream)),
+                    "permute_rows launch");
+}
+
+size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int Ck, int Bq) {
+  if (B <= 0 || H <= 0 || N <= 0 || Cq <= 0 || Ck <= 0 || Cq > SA_MAX_CLUSTERS || Ck > SA_MAX_CLUSTERS ||
+      (Bq != 64 && Bq != 128))
+    return 0;
+  return sa::cluster_fwd_workspace_bytes(B * H, N, Cq, Ck, Bq);
+}
+
+int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
+                            const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck, const uint8_t* mask,
+                            int Bq, double scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!q_offsets || !k_offsets || !mask || !workspace) return fail(SA_ERR_INVALID_ARG, "cluster_fwd: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: only SA_BF16 tensors are supported");
+  if (Cq <= 0 || Ck <= 0 || Cq > N || Ck > N) return fail(SA_ERR_INVALID_ARG, "cluster_fwd: cluster counts must lie in [1, N]");
+  if (Cq > SA_MAX_CLUSTERS || Ck > SA_MAX_CLUSTERS)
+    return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: cluster counts exceed %d", SA_MAX_CLUSTERS);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(SA_ERR_INVALID_ARG, "cluster_fwd: workspace must be 256-byte aligned");
+  const size_t need = sparse_attn_cluster_fwd_workspace_size(B, H, N, Cq, Ck, Bq);
+  if (workspace_bytes < need)
+    return fail(SA_ERR_INVALID_ARG, "cluster_fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                need);
+  if ((long long)B * H * sa::cluster_max_tiles(N, Cq, Bq) > 0x7fffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: too many query tiles");
+  return hip_status(sa::launch_cluster_fwd(q, k, v, B * H, N, d, q_offsets, Cq, k_offsets, Ck, mask, Bq, scale, o, lse,
+                                           workspace, static_cast<hipStream_t>(stream)),
+                    "cluster_fwd launch");
 }
 
 int sparse_attn_pattern_mask(int patterns, int window, int band, int period, int B, int H, int N, int Bq, int Bk,

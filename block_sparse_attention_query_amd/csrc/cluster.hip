@@ -1,0 +1,768 @@
+// Semantic-aware permutation with centroid Top-p and attention over variable-size blocks (gfx950).
+//
+// Page "Sparse VideoGen2: Accelerate Video Generation with Sparse Attention via Semantic-Aware
+// Permutation" (gist.science summary), section "2. 手法":
+//   A. k-means clusters of Q and of K; tokens permuted so that every cluster is contiguous; the
+//      output, permuted back, equals attention in the original order.
+//   B. scores between cluster centroids, clusters taken in descending order of estimated score
+//      until the running sum reaches p.
+//   C. attention over variable-size blocks: dense contiguous queries, sparse key/value loads.
+// Kernels:
+//   km_init / km_assign / km_rank / km_scan / km_scatter / km_update   Lloyd's k-means; the
+//       assignment runs on bf16 MFMA with every centroid split into a high and a low bf16 part
+//       (about 16 mantissa bits), the permutation is a stable counting sort, and the update is a
+//       float64 mean over each cluster's contiguous run of the permuted order (deterministic).
+//   cluster_select    float64 centroid scores, size-weighted softmax, sort, Top-p cut.
+//   permute_rows      gather (or scatter) of [N, d] rows by a permutation.
+//   cluster_tiles     query tiles of up to BQ rows inside each query cluster.
+//   attn_var          flash attention of one query tile over the concatenated keys of its kept
+//                     key clusters: every lane's DMA fetches its own key row, so 64-key tiles are
+//                     filled across cluster boundaries and only the stream's last tile is partial.
+#include <algorithm>
+
+#include "attn_tiles.h"
+
+namespace sa {
+
+constexpr int KM_MAXC = 1024;  // clusters per head
+constexpr int KM_CH = 256;     // tokens per chunk of the counting sort
+
+// Exclusive prefix sum of v over the NT threads of the workgroup; returns this thread's prefix
+// and writes the total to *total. scratch holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int s = scratch[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  *total = tot;
+  __syncthreads();  // scratch may be reused by the caller
+  return base + inc - v;
+}
+
+// ---------------------------------------------------------------- k-means
+
+// Operands of the assignment for centroid c of head bh: high and low bf16 parts (padded rows
+// past C are zero) and the fp32 squared norm (+inf for padded rows, which are never chosen).
+template <int D>
+__device__ __forceinline__ void km_write_operands(const float vch, int bh, int c, int C, int CP, __bf16* chi,
+                                                  __bf16* clo, float* cn, float* red) {
+  const int ch = threadIdx.x;
+  const __bf16 hi = (__bf16)vch;
+  const __bf16 lo = (__bf16)(vch - (float)hi);
+  chi[((size_t)bh * CP + c) * D + ch] = hi;
+  clo[((size_t)bh * CP + c) * D + ch] = lo;
+  float sq = vch * vch;
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if ((ch & 63) == 0) red[ch >> 6] = sq;
+  __syncthreads();
+  if (ch == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) s += red[w];
+    cn[(size_t)bh * CP + c] = c < C ? s : INFINITY;
+  }
+}
+
+// Grid (BH, CP), D threads: centroid c starts at token floor((2c + 1) N / (2C)), or at init.
+template <int D>
+__global__ __launch_bounds__(D) void km_init_kernel(const uint16_t* __restrict__ x, const float* __restrict__ init,
+                                                    int N, int C, int CP, float* __restrict__ cen,
+                                                    __bf16* __restrict__ chi, __bf16* __restrict__ clo,
+                                                    float* __restrict__ cn) {
+  __shared__ float red[D / 64];
+  const int bh = blockIdx.x, c = blockIdx.y, ch = threadIdx.x;
+  float v = 0.f;
+  if (c < C) {
+    if (init != nullptr) {
+      v = init[((size_t)bh * C + c) * D + ch];
+    } else {
+      const long long tok = ((2LL * c + 1) * N) / (2LL * C);
+      v = __uint_as_float((uint32_t)x[((size_t)bh * N + tok) * D + ch] << 16);
+    }
+    cen[((size_t)bh * C + c) * D + ch] = v;
+  }
+  km_write_operands<D>(v, bh, c, C, CP, chi, clo, cn, red);
+}
+
+// Grid (BH, ceil(N / 256)), 4 waves of 64 tokens (two sets of 32). Centroids stream through LDS
+// 64 at a time; per 32-centroid tile, S^T = (C_hi + C_lo) X^T on bf16 MFMA (element i of lane j:
+// centroid 8 (i / 4) + 4 (j / 32) + i % 4 of the tile, token j % 32), then dist = |c|^2 - 2 <x, c>.
+// Each lane visits its centroids in ascending order and keeps the first strict minimum; the two
+// halves of a token's centroids are merged with the lower index on equality.
+template <int D>
+__global__ __launch_bounds__(256) void km_assign_kernel(const uint16_t* __restrict__ x, const __bf16* __restrict__ chi,
+                                                        const __bf16* __restrict__ clo, const float* __restrict__ cn,
+                                                        int N, int CP, int32_t* __restrict__ labels) {
+  constexpr int CT = 64;               // centroids per LDS stage
+  constexpr int RB = 2 * D + 16;       // padded LDS row (bytes)
+  __shared__ __attribute__((aligned(16))) char hs[CT * RB];
+  __shared__ __attribute__((aligned(16))) char ls[CT * RB];
+  __shared__ float cns[KM_MAXC];
+  const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  for (int c = tid; c < CP; c += 256) cns[c] = cn[(size_t)bh * CP + c];
+  const uint16_t* xh = x + (size_t)bh * N * D;
+  bf16x8 xf[2][D / 16];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int t = blockIdx.y * 256 + wave * 64 + s * 32 + ln;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      xf[s][j] = __builtin_bit_cast(bf16x8, t < N ? *reinterpret_cast<const uint4*>(xh + (size_t)t * D + 16 * j + 8 * hf)
+                                                  : make_uint4(0, 0, 0, 0));
+  }
+  float best[2] = {INFINITY, INFINITY};
+  int bidx[2] = {0, 0};
+  const char* hg = reinterpret_cast<const char*>(chi + (size_t)bh * CP * D);
+  const char* lg = reinterpret_cast<const char*>(clo + (size_t)bh * CP * D);
+  for (int c0 = 0; c0 < CP; c0 += CT) {
+    const int rows = min(CT, CP - c0);
+    __syncthreads();  // the previous stage has been read (and cns is resident)
+    for (int e = tid; e < rows * (2 * D / 16); e += 256) {
+      const int r = e / (2 * D / 16), k = e % (2 * D / 16);
+      *reinterpret_cast<uint4*>(hs + r * RB + k * 16) = *reinterpret_cast<const uint4*>(hg + (size_t)(c0 + r) * 2 * D + k * 16);
+      *reinterpret_cast<uint4*>(ls + r * RB + k * 16) = *reinterpret_cast<const uint4*>(lg + (size_t)(c0 + r) * 2 * D + k * 16);
+    }
+    __syncthreads();
+    for (int ct = 0; ct < rows; ct += 32) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[s][i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const int off = (ct + ln) * RB + (16 * j + 8 * hf) * 2;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(hs + off);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(ls + off);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[s][j], acc[s], 0, 0, 0);
+          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[s][j], acc[s], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = c0 + ct + 8 * (i >> 2) + 4 * hf + (i & 3);
+        const float cnv = cns[c];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float dv = fmaf(-2.f, acc[s][i], cnv);
+          if (dv < best[s]) {
+            best[s] = dv;
+            bidx[s] = c;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const float pb = __shfl_xor(best[s], 32, 64);
+    const int pi = __shfl_xor(bidx[s], 32, 64);
+    if (pb < best[s] || (pb == best[s] && pi < bidx[s])) bidx[s] = pi;
+    const int t = blockIdx.y * 256 + wave * 64 + s * 32 + ln;
+    if (hf == 0 && t < N) labels[(size_t)bh * N + t] = bidx[s];
+  }
+}
+
+// Counting sort, pass 1. Grid (BH, ceil(N / 256)): for every token, the number of earlier tokens
+// of its chunk with the same label; per chunk, the count of every label (all C of them).
+__global__ __launch_bounds__(KM_CH) void km_rank_kernel(const int32_t* __restrict__ labels, int N, int C, int nch,
+                                                       int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+  __shared__ int lab[KM_CH];
+  __shared__ int cnt[KM_MAXC];
+  const int bh = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x;
+  const int t = ch * KM_CH + tid;
+  for (int c = tid; c < C; c += KM_CH) cnt[c] = 0;
+  const int my = t < N ? labels[(size_t)bh * N + t] : -1;
+  lab[tid] = my;
+  __syncthreads();
+  int r = 0;
+  for (int u = 0; u < tid; ++u) r += lab[u] == my;
+  if (t < N) {
+    rank[(size_t)bh * N + t] = r;
+    atomicAdd(&cnt[my], 1);  // counts only: the order of the additions does not matter
+  }
+  __syncthreads();
+  int32_t* hrow = hist + ((size_t)bh * nch + ch) * C;
+  for (int c = tid; c < C; c += KM_CH) hrow[c] = cnt[c];
+}
+
+// Pass 2. Grid BH, 1024 threads (thread = label): exclusive prefix of every label's chunk counts
+// over the chunks (in place), then offsets[c] = the exclusive prefix of the label totals.
+__global__ __launch_bounds__(KM_MAXC) void km_scan_kernel(int32_t* __restrict__ hist, int C, int nch,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int scratch[KM_MAXC / 64];
+  const int bh = blockIdx.x, c = threadIdx.x;
+  int run = 0;
+  if (c < C) {
+    int32_t* h = hist + (size_t)bh * nch * C + c;
+    for (int k = 0; k < nch; ++k) {
+      const int v = h[(size_t)k * C];
+      h[(size_t)k * C] = run;
+      run += v;
+    }
+  }
+  int total;
+  const int ex = block_exclusive_scan<KM_MAXC>(c < C ? run : 0, scratch, &total);
+  if (c < C) offsets[(size_t)bh * (C + 1) + c] = ex;
+  if (c == 0) offsets[(size_t)bh * (C + 1) + C] = total;
+}
+
+// Pass 3. Grid (BH, ceil(N / 256)): perm[offsets[l] + chunk base[l] + rank] = token.
+__global__ __launch_bounds__(KM_CH) void km_scatter_kernel(const int32_t* __restrict__ labels,
+                                                          const int32_t* __restrict__ rank,
+                                                          const int32_t* __restrict__ hist,
+                                                          const int32_t* __restrict__ offsets, int N, int C, int nch,
+                                                          int32_t* __restrict__ perm) {
+  const int bh = blockIdx.x, ch = blockIdx.y;
+  const int t = ch * KM_CH + threadIdx.x;
+  if (t >= N) return;
+  const int l = labels[(size_t)bh * N + t];
+  const int pos = offsets[(size_t)bh * (C + 1) + l] + hist[((size_t)bh * nch + ch) * C + l] + rank[(size_t)bh * N + t];
+  perm[(size_t)bh * N + pos] = t;
+}
+
+// Grid (BH, CP), D threads: centroid c = the float64 mean of its tokens, summed in permuted order
+// (an empty cluster keeps its centroid), then its MFMA operands.
+template <int D>
+__global__ __launch_bounds__(D) void km_update_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ offsets, int N, int C, int CP,
+                                                      float* __restrict__ cen, __bf16* __restrict__ chi,
+                                                      __bf16* __restrict__ clo, float* __restrict__ cn) {
+  __shared__ float red[D / 64];
+  const int bh = blockIdx.x, c = blockIdx.y, ch = threadIdx.x;
+  float v = 0.f;
+  if (c < C) {
+    const int o0 = offsets[(size_t)bh * (C + 1) + c], o1 = offsets[(size_t)bh * (C + 1) + c + 1];
+    float* cp = cen + ((size_t)bh * C + c) * D + ch;
+    if (o1 > o0) {
+      const uint16_t* xh = x + (size_t)bh * N * D + ch;
+      const int32_t* pp = perm + (size_t)bh * N;
+      double acc = 0.0;
+      int m = o0;
+      for (; m + 4 <= o1; m += 4) {  // four independent loads in flight, summed in order
+        const int t0 = pp[m], t1 = pp[m + 1], t2 = pp[m + 2], t3 = pp[m + 3];
+        const uint32_t a = xh[(size_t)t0 * D], b = xh[(size_t)t1 * D], e = xh[(size_t)t2 * D], f = xh[(size_t)t3 * D];
+        acc += (double)__uint_as_float(a << 16);
+        acc += (double)__uint_as_float(b << 16);
+        acc += (double)__uint_as_float(e << 16);
+        acc += (double)__uint_as_float(f << 16);
+      }
+      for (; m < o1; ++m) acc += (double)__uint_as_float((uint32_t)xh[(size_t)pp[m] * D] << 16);
+      v = (float)(acc / (double)(o1 - o0));
+      *cp = v;
+    } else {
+      v = *cp;
+    }
+  }
+  km_write_operands<D>(v, bh, c, C, CP, chi, clo, cn, red);
+}
+
+// ---------------------------------------------------------------- centroid Top-p
+
+// Grid (BH, Cq), 256 threads. Row i: S_ij = scale <cq_i, ck_j> (float64), weights
+// n_j exp(S_ij - max) over the non-empty key clusters, probabilities = weights / their sum;
+// bitonic sort by (probability descending, index ascending); the kept length is
+// min(#non-empty, max(1, m*)) with m* the first prefix whose sequential running sum reaches p.
+__global__ __launch_bounds__(256) void cluster_select_kernel(const float* __restrict__ cq, const float* __restrict__ ck,
+                                                             const int32_t* __restrict__ koff, int Cq, int Ck, int d,
+                                                             double scale, double p, double* __restrict__ probs,
+                                                             uint8_t* __restrict__ mask) {
+  __shared__ double qrow[128];
+  __shared__ double pv[KM_MAXC];
+  __shared__ int pi[KM_MAXC];
+  __shared__ double red[4];
+  __shared__ int keep_len;
+  const int bh = blockIdx.x, i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < d; e += 256) qrow[e] = (double)cq[((size_t)bh * Cq + i) * d + e];
+  int np = 1;
+  while (np < Ck) np <<= 1;
+  __syncthreads();
+  double lmax = -INFINITY;
+  for (int j = tid; j < Ck; j += 256) {
+    const float* kr = ck + ((size_t)bh * Ck + j) * d;
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s = fma(qrow[e], (double)kr[e], s);
+    s *= scale;
+    const int n = koff[(size_t)bh * (Ck + 1) + j + 1] - koff[(size_t)bh * (Ck + 1) + j];
+    pv[j] = n > 0 ? s : -INFINITY;
+    lmax = fmax(lmax, pv[j]);
+  }
+  for (int o = 32; o > 0; o >>= 1) lmax = fmax(lmax, __shfl_xor(lmax, o, 64));
+  if (lane == 0) red[wave] = lmax;
+  __syncthreads();
+  const double M = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  __syncthreads();
+  double lsum = 0.0;
+  for (int j = tid; j < Ck; j += 256) {
+    const int n = koff[(size_t)bh * (Ck + 1) + j + 1] - koff[(size_t)bh * (Ck + 1) + j];
+    const double w = n > 0 ? (double)n * exp(pv[j] - M) : 0.0;
+    pv[j] = w;
+    lsum += w;
+  }
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+  for (int j = tid; j < np; j += 256) {
+    if (j < Ck) {
+      pv[j] /= tot;
+      if (probs != nullptr) probs[((size_t)bh * Cq + i) * Ck + j] = pv[j];
+    } else {
+      pv[j] = -1.0;  // padding sorts last
+    }
+    pi[j] = j;
+  }
+  // bitonic sort into descending probability, ascending index on equality
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      __syncthreads();
+      for (int e = tid; e < np; e += 256) {
+        const int f = e ^ jj;
+        if (f > e) {
+          const bool up = (e & k) == 0;  // this run is ordered "first before"
+          const double a = pv[e], b = pv[f];
+          const int ia = pi[e], ib = pi[f];
+          const bool a_first = a > b || (a == b && ia < ib);
+          if (a_first != up) {
+            pv[e] = b;
+            pv[f] = a;
+            pi[e] = ib;
+            pi[f] = ia;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int nnz = 0, mstar = Ck;
+    double run = 0.0;
+    bool hit = p <= 0.0;
+    if (hit) mstar = 0;
+    for (int s = 0; s < Ck; ++s) {
+      if (pv[s] > 0.0) ++nnz;
+      if (!hit) {
+        run += pv[s];
+        if (run >= p) {
+          hit = true;
+          mstar = s + 1;
+        }
+      }
+    }
+    keep_len = min(nnz, max(1, mstar));
+  }
+  uint8_t* mrow = mask + ((size_t)bh * Cq + i) * Ck;
+  for (int j = tid; j < Ck; j += 256) mrow[j] = 0;
+  __syncthreads();
+  for (int s = tid; s < keep_len; s += 256) mrow[pi[s]] = 1;
+}
+
+// ---------------------------------------------------------------- permutation of rows
+
+// One thread per 16-byte piece: out[t'] = x[perm[t']] (gather) or out[perm[t']] = x[t'] (scatter).
+__global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restrict__ x, const int32_t* __restrict__ perm,
+                                                           int N, int row_bytes, int inverse, long long pieces,
+                                                           char* __restrict__ out) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= pieces) return;
+  const int per = row_bytes / 16;
+  const long long row = e / per;
+  const int k = (int)(e % per);
+  const long long bh = row / N;
+  const int t = (int)(row % N);
+  const long long src = inverse ? row : bh * N + perm[row];
+  const long long dst = inverse ? bh * N + perm[row] : row;
+  (void)t;
+  *reinterpret_cast<uint4*>(out + dst * row_bytes + k * 16) = *reinterpret_cast<const uint4*>(x + src * row_bytes + k * 16);
+}
+
+// ---------------------------------------------------------------- variable-size blocks
+
+// Grid BH, 1024 threads (thread = query cluster): query tiles (cluster, first row, rows) of at
+// most BQ rows inside every cluster of the permuted query order.
+__global__ __launch_bounds__(KM_MAXC) void cluster_tiles_kernel(const int32_t* __restrict__ qoff, int Cq, int BQ,
+                                                               int max_tiles, int4* __restrict__ tiles,
+                                                               int32_t* __restrict__ ntiles) {
+  __shared__ int scratch[KM_MAXC / 64];
+  const int bh = blockIdx.x, i = threadIdx.x;
+  int o0 = 0, n = 0;
+  if (i < Cq) {
+    o0 = qoff[(size_t)bh * (Cq + 1) + i];
+    n = qoff[(size_t)bh * (Cq + 1) + i + 1] - o0;
+  }
+  const int nt = (n + BQ - 1) / BQ;
+  int total;
+  const int base = block_exclusive_scan<KM_MAXC>(nt, scratch, &total);
+  for (int t = 0; t < nt; ++t)
+    tiles[(size_t)bh * max_tiles + base + t] = make_int4(i, o0 + t * BQ, min(BQ, n - t * BQ), 0);
+  if (i == 0) ntiles[bh] = total;
+}
+
+// DMA of key tile t of the stream (and the matching value rows) into dst (K) and dst + TILE (V).
+// Stream position pos lies in the range e with cum[e] <= pos < cum[e + 1]; the lane's cursor
+// cur[u] only moves forward because positions grow with t.
+template <int D, int BQ>
+__device__ __forceinline__ void var_gather(const char* __restrict__ kbase, const char* __restrict__ vbase, int t,
+                                           int L, const __attribute__((address_space(3))) int* cum,
+                                           const __attribute__((address_space(3))) int* rstart,
+                                           const int (&trow)[DCfg<D, BQ>::PER_WAVE],
+                                           const uint32_t (&choff)[DCfg<D, BQ>::PER_WAVE],
+                                           int (&cur)[DCfg<D, BQ>::PER_WAVE], int wave, lchar* dst) {
+  using C = DCfg<D, BQ>;
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u) {
+    const int pos = min(t * BK + trow[u], L - 1);
+    while (cum[cur[u] + 1] <= pos) ++cur[u];
+    const size_t off = (size_t)(rstart[cur[u]] + pos - cum[cur[u]]) * C::ROWB + choff[u];
+    __builtin_amdgcn_global_load_lds(kbase + off, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + off, dst + C::TILE + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
+  }
+}
+
+// One workgroup per query tile (i, qs, qc) of head bh. The key stream of cluster i is the
+// concatenation, in ascending cluster order, of the key ranges [koff[j], koff[j + 1]) of its kept
+// clusters j; cum[] holds the stream position where each range starts. Key tile t covers stream
+// positions 64 t .. 64 t + 63: the DMA lane that fills row r of the tile follows a cursor through
+// the ranges (positions only grow, so it never moves back) and loads key row
+// rstart[e] + pos - cum[e]. Positions past the stream's end are clamped to its last key and get
+// score -inf. The S^T / PV products, the tile layout and the lazy rescale are the forward
+// kernel's.
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restrict__ q, const void* __restrict__ k,
+                                                             const void* __restrict__ v, int N,
+                                                             const int4* __restrict__ tiles,
+                                                             const int32_t* __restrict__ ntiles, int max_tiles,
+                                                             const int32_t* __restrict__ koff, int Cq, int Ck,
+                                                             const int32_t* __restrict__ kidx,
+                                                             const int32_t* __restrict__ kcnt, float c_log2,
+                                                             void* __restrict__ o, float* __restrict__ lse) {
+  using C = DCfg<D, BQ>;
+  constexpr int NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char buf1_[2 * C::TILE];
+  __shared__ int rstart[KM_MAXC];
+  __shared__ int cum[KM_MAXC + 1];
+  __shared__ int scratch[NT / 64];
+  lchar* const buf0 = (lchar*)buf0_;
+  lchar* const buf1 = (lchar*)buf1_;
+
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = w / max_tiles, tile = w % max_tiles;
+  if (tile >= ntiles[bh]) return;  // uniform over the workgroup
+  const int4 tl = tiles[(size_t)bh * max_tiles + tile];
+  const int ci = tl.x, qs = tl.y, qc = tl.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+
+  // the key ranges of the kept clusters and their stream positions
+  const int cnt = kcnt[(size_t)bh * Cq + ci];
+  const int32_t* list = kidx + ((size_t)bh * Cq + ci) * Ck;
+  const int32_t* ko = koff + (size_t)bh * (Ck + 1);
+  constexpr int PT = (KM_MAXC + NT - 1) / NT;
+  int sz[PT], lsum = 0;
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = tid * PT + u;
+    sz[u] = 0;
+    if (e < cnt) {
+      const int j = list[e];
+      rstart[e] = ko[j];
+      sz[u] = ko[j + 1] - ko[j];
+    }
+    lsum += sz[u];
+  }
+  int L;
+  int run = block_exclusive_scan<NT>(lsum, scratch, &L);
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int e = tid * PT + u;
+    if (e < cnt) cum[e] = run;
+    run += sz[u];
+  }
+  if (tid == 0) cum[cnt] = L;
+  __syncthreads();
+  const int ntk = (L + BK - 1) / BK;
+
+  const size_t head_off = (size_t)bh * N * D * 2;
+  const char* qbase = static_cast<const char*>(q) + head_off;
+  const char* kbase = static_cast<const char*>(k) + head_off;
+  const char* vbase = static_cast<const char*>(v) + head_off;
+  // this lane's DMA pieces: tile row trow[u], byte offset choff[u] inside the row
+  uint32_t doff[C::PER_WAVE];
+  dma_offsets<D, BQ>(wave, lane, doff);
+  int trow[C::PER_WAVE], cur[C::PER_WAVE];
+  uint32_t choff[C::PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u) {
+    trow[u] = ((wave * C::PER_WAVE + u) * 1024 + lane * 16) / C::ROWB;
+    choff[u] = doff[u] - (uint32_t)(trow[u] * C::ROWB);
+    cur[u] = 0;
+  }
+  typedef __attribute__((address_space(3))) const int lint;
+  lint* cum_l = (lint*)cum;
+  lint* rst_l = (lint*)rstart;
+  if (ntk > 0) var_gather<D, BQ>(kbase, vbase, 0, L, cum_l, rst_l, trow, choff, cur, wave, buf0);
+
+  const int qrow = qs + wave * 32 + ln;
+  const bool qvalid = wave * 32 + ln < qc;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+    qf[j] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * j + 8 * hf) * 2)
+                                              : make_uint4(0, 0, 0, 0));
+  int koffs[D / 16];
+  {
+    const int sw = kv_swz<D>(ln);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) koffs[j] = ln * C::ROWB + (((2 * j + hf) ^ sw) << 4);
+  }
+  int voff[D / 32][2];
+  {
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int half = grp >> 1, gsub = grp & 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 8 * u + 4 * half + (i16 >> 2);
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) {
+        const int chunk = 4 * r + 2 * gsub + ((i16 & 3) >> 1);
+        voff[r][u] = row * C::ROWB + ((chunk ^ kv_swz<D>(row)) << 4) + (i16 & 1) * 8;
+      }
+    }
+  }
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (int t = 0; t < ntk; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t is resident; every wave is done with tile t - 1
+    if (t + 1 < ntk) var_gather<D, BQ>(kbase, vbase, t + 1, L, cum_l, rst_l, trow, choff, cur, wave, (t & 1) ? buf0 : buf1);
+    const lchar* kt = (t & 1) ? buf1 : buf0;
+    lchar* vt = ((t & 1) ? buf1 : buf0) + C::TILE;
+    f32x16 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.f;
+      s1[i] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j]);
+      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j] + 32 * C::ROWB);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], s1, 0, 0, 0);
+    }
+    if (t * BK + BK > L) {  // stream positions past the end
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pos = t * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (pos >= L) s0[i] = -INFINITY;
+        if (pos + 32 >= L) s1[i] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = partner32_max(mx) * c_log2;
+    if (__ballot(mx > m_run + 8.f)) {  // lazy rescale: weights stay below 2^8 between raises
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pb[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
+        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
+      }
+      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+    }
+    l_run += rs;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
+        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
+      }
+  }
+  __syncthreads();  // every wave is done with the K / V buffers before they stage the output
+
+  // epilogue: O = O^T / l, staged through LDS (two waves per buffer pair) for row-contiguous stores
+  const float l_tot = partner32_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  lchar* ol = ((wave & 1) ? buf1 : buf0) + (wave >> 1) * 32 * C::OROW;
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int ch = 32 * r + 8 * a + 4 * hf;
+      const u32x2 wv = {pack_bf16(oacc[r][4 * a] * inv, oacc[r][4 * a + 1] * inv),
+                        pack_bf16(oacc[r][4 * a + 2] * inv, oacc[r][4 * a + 3] * inv)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(ol + ln * C::OROW + ch * 2) = wv;
+    }
+  __syncthreads();
+  constexpr int CH16 = D * 2 / 16;
+  char* obase = static_cast<char*>(o) + head_off;
+#pragma unroll
+  for (int e = lane; e < 32 * CH16; e += 64) {
+    const int r = e / CH16, cc = e % CH16;
+    if (wave * 32 + r < qc)
+      *reinterpret_cast<u32x4*>(obase + (size_t)(qs + wave * 32 + r) * D * 2 + cc * 16) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ol + r * C::OROW + cc * 16);
+  }
+  if (lse != nullptr && hf == 0 && qvalid)
+    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+}
+
+// ---------------------------------------------------------------- workspaces and launchers
+
+namespace {
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+int pad32(int c) { return (c + 31) / 32 * 32; }
+}  // namespace
+
+size_t kmeans_workspace_bytes(int BH, int N, int d, int C) {
+  const size_t CP = (size_t)pad32(C), nch = (size_t)(N + KM_CH - 1) / KM_CH;
+  return 2 * al256((size_t)BH * CP * d * 2) + al256((size_t)BH * CP * 4) + al256((size_t)BH * N * 4) +
+         al256((size_t)BH * nch * C * 4);
+}
+
+hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, const float* init, float* cen,
+                         int32_t* labels, int32_t* perm, int32_t* offsets, void* ws, hipStream_t stream) {
+  const int CP = pad32(C), nch = (N + KM_CH - 1) / KM_CH;
+  char* p = static_cast<char*>(ws);
+  __bf16* chi = reinterpret_cast<__bf16*>(p);
+  p += al256((size_t)BH * CP * d * 2);
+  __bf16* clo = reinterpret_cast<__bf16*>(p);
+  p += al256((size_t)BH * CP * d * 2);
+  float* cn = reinterpret_cast<float*>(p);
+  p += al256((size_t)BH * CP * 4);
+  int32_t* rank = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)BH * N * 4);
+  int32_t* hist = reinterpret_cast<int32_t*>(p);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  hipError_t e;
+#define SA_KM(D_)                                                                                                  \
+  hipLaunchKernelGGL((km_init_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(D_), 0, stream, xs, init, N, C, CP, \
+                     cen, chi, clo, cn);                                                                           \
+  if ((e = hipGetLastError()) != hipSuccess) return e;                                                             \
+  for (int it = 0; it < iters; ++it) {                                                                             \
+    hipLaunchKernelGGL((km_assign_kernel<D_>), dim3((unsigned)BH, (unsigned)((N + 255) / 256)), dim3(256), 0, stream, \
+                       xs, chi, clo, cn, N, CP, labels);                                                           \
+    hipLaunchKernelGGL(km_rank_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, N, C, nch, \
+                       rank, hist);                                                                                \
+    hipLaunchKernelGGL(km_scan_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, hist, C, nch, offsets);       \
+    hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, rank,  \
+                       hist, offsets, N, C, nch, perm);                                                            \
+    hipLaunchKernelGGL((km_update_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(D_), 0, stream, xs, perm,     \
+                       offsets, N, C, CP, cen, chi, clo, cn);                                                      \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                                           \
+  }
+  if (d == 128) {
+    SA_KM(128)
+  } else if (d == 64) {
+    SA_KM(64)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef SA_KM
+  return hipSuccess;
+}
+
+hipError_t launch_cluster_select(const float* cq, const float* ck, const int32_t* koff, int BH, int Cq, int Ck, int d,
+                                 double scale, double p, double* probs, uint8_t* mask, hipStream_t stream) {
+  hipLaunchKernelGGL(cluster_select_kernel, dim3((unsigned)BH, (unsigned)Cq), dim3(256), 0, stream, cq, ck, koff, Cq,
+                     Ck, d, scale, p, probs, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const void* x, const int32_t* perm, int BH, int N, int row_bytes, int inverse,
+                               void* out, hipStream_t stream) {
+  const long long pieces = (long long)BH * N * (row_bytes / 16);
+  hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const char*>(x), perm, N, row_bytes, inverse, pieces, static_cast<char*>(out));
+  return hipGetLastError();
+}
+
+int cluster_max_tiles(int N, int Cq, int Bq) { return (N + Bq - 1) / Bq + Cq; }
+
+size_t cluster_fwd_workspace_bytes(int BH, int N, int Cq, int Ck, int Bq) {
+  const size_t mt = (size_t)cluster_max_tiles(N, Cq, Bq);
+  return al256((size_t)BH * mt * 16) + al256((size_t)BH * 4) + al256((size_t)BH * Cq * Ck * 4) +
+         al256((size_t)BH * Cq * 4);
+}
+
+hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
+
+hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int BH, int N, int d, const int32_t* qoff,
+                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, int Bq, double scale, void* o,
+                              float* lse, void* ws, hipStream_t stream) {
+  const int mt = cluster_max_tiles(N, Cq, Bq);
+  char* p = static_cast<char*>(ws);
+  int4* tiles = reinterpret_cast<int4*>(p);
+  p += al256((size_t)BH * mt * 16);
+  int32_t* nt = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)BH * 4);
+  int32_t* kidx = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)BH * Cq * Ck * 4);
+  int32_t* kcnt = reinterpret_cast<int32_t*>(p);
+  hipLaunchKernelGGL(cluster_tiles_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, qoff, Cq, Bq, mt, tiles, nt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_compact(mask, BH * Cq, Ck, kidx, kcnt, stream)) != hipSuccess) return e;
+  const float c_log2 = (float)(scale * 1.4426950408889634);
+  const dim3 grid((unsigned)((size_t)BH * mt));
+#define SA_VAR(D_, BQ_)                                                                                            \
+  if (d == D_ && Bq == BQ_) {                                                                                      \
+    hipLaunchKernelGGL((attn_var_kernel<D_, BQ_>), grid, dim3(DCfg<D_, BQ_>::NT), 0, stream, q, k, v, N, tiles, nt,  \
+                       mt, koff, Cq, Ck, kidx, kcnt, c_log2, o, lse);                                              \
+    return hipGetLastError();                                                                                      \
+  }
+  SA_VAR(128, 128)
+  SA_VAR(128, 64)
+  SA_VAR(64, 128)
+  SA_VAR(64, 64)
+#undef SA_VAR
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

@@ -54,6 +54,7 @@ extern "C" {
 /* Supported values (others return SA_ERR_UNSUPPORTED): d in {64, 128}; Bq in {64, 128};
  * Bk = 64 for sparse_attn_fwd (pooling accepts Bq, Bk in {64, 128}); nKB <= 8192. */
 #define SA_MAX_NKB 8192
+#define SA_MAX_CLUSTERS 1024  /* clusters per head for the semantic-aware permutation calls */
 
 /*
  * Block mean pooling of Q and K ([SVG2] "1. 問題定義": consecutive tokens grouped into blocks,
@@ -236,6 +237,89 @@ size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int 
 int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void* o, int dtype, int B, int H, int N,
                               int d, int Bq, double scale, int probes, double ridge, float* a_out, float* exact_out,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Semantic-aware permutation ([SVG2] "2. 手法" A, B, C): tokens are grouped by k-means on Q and on
+ * K, permuted so that every cluster is contiguous, clusters of keys are chosen per query cluster
+ * by a Top-p over centroid scores, and attention runs over the variable-size blocks that the
+ * clusters form. Permuting the output back gives attention in the original order.
+ */
+
+/* Bytes of device scratch sparse_attn_kmeans needs (0 if the sizes are invalid). */
+size_t sparse_attn_kmeans_workspace_size(int B, int H, int N, int d, int C);
+
+/*
+ * Lloyd's k-means of the N token rows of x, per (b, h), into C clusters.
+ *   x          device, [B, H, N, d] SA_BF16.
+ *   init       device or NULL, [B, H, C, d] float32 starting centroids (a warm start); NULL starts
+ *              centroid c at token floor((2c + 1) N / (2C)).
+ *   iters      >= 1 iterations of: assign every token to the centroid with the smallest
+ *              |mu|^2 - 2 <x, mu> (the order of |x - mu|^2; the lowest index on a tie; the
+ *              products use the bf16 token and the centroid split into two bf16 parts, summed
+ *              in fp32), then move every centroid to the float64 mean of its tokens (an empty
+ *              cluster keeps its centroid).
+ *   centroids  device out, [B, H, C, d] float32: after the last update.
+ *   labels     device out, [B, H, N] int32: the last assignment.
+ *   perm       device out, [B, H, N] int32: the stable sort of tokens by label; perm[t'] is the
+ *              token at permuted position t'.
+ *   offsets    device out, [B, H, C + 1] int32: cluster c occupies [offsets[c], offsets[c + 1]).
+ *   workspace  device scratch of at least sparse_attn_kmeans_workspace_size() bytes, 256-byte
+ *              aligned; overwritten.
+ * d in {64, 128}, 1 <= C <= min(N, SA_MAX_CLUSTERS). Deterministic.
+ */
+int sparse_attn_kmeans(const void* x, int dtype, int B, int H, int N, int d, int C, int iters, const float* init,
+                       float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Centroid Top-p ([SVG2] "2. 手法" B). For query cluster i the estimated attention mass of key
+ * cluster j is n_j exp(S_ij) normalised over j, with S_ij = scale <cq_i, ck_j> (float64) and n_j
+ * the cluster's size (empty clusters have none). Clusters are taken in descending mass (the lower
+ * index first on equality) until the sequential running sum reaches p; at least one and never an
+ * empty cluster is taken.
+ *   cq, ck      device, [B, H, Cq, d] and [B, H, Ck, d] float32 centroids.
+ *   k_offsets   device, [B, H, Ck + 1] int32: the key clusters' offsets (their sizes).
+ *   probs       device out or NULL, [B, H, Cq, Ck] float64 masses.
+ *   mask        device out, [B, H, Cq, Ck] uint8, 1 = keep.
+ * d in {64, 128}; Cq, Ck <= SA_MAX_CLUSTERS; 0 <= p <= 1.
+ */
+int sparse_attn_cluster_select(const float* cq, const float* ck, const int32_t* k_offsets, int B, int H, int Cq, int Ck,
+                               int d, double scale, double p, double* probs, uint8_t* mask, void* stream);
+
+/*
+ * Row permutation: out[b, h, t', :] = x[b, h, perm[t'], :] (inverse = 0), or
+ * out[b, h, perm[t'], :] = x[b, h, t', :] (inverse != 0).
+ *   x, out   device, [B, H, N, d] of `dtype`, 16-byte aligned, not aliased.
+ *   perm     device, [B, H, N] int32, a permutation of 0..N-1 per (b, h) (not checked).
+ */
+int sparse_attn_permute_rows(const void* x, int dtype, int B, int H, int N, int d, const int32_t* perm, int inverse,
+                             void* out, void* stream);
+
+/* Bytes of device scratch sparse_attn_cluster_fwd needs (0 if the sizes are invalid). */
+size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int Ck, int Bq);
+
+/*
+ * Attention over variable-size blocks ([SVG2] "2. 手法" C), in the permuted order: every query of
+ * query cluster i (rows [q_offsets[i], q_offsets[i + 1])) attends to exactly the keys of the key
+ * clusters j with mask[i][j] = 1 (rows [k_offsets[j], k_offsets[j + 1])). Arithmetic as in
+ * sparse_attn_fwd; a query cluster with no kept key gets O = 0 and LSE = -inf. Queries run in
+ * tiles of Bq rows inside each cluster; the kept keys are gathered into 64-row tiles across
+ * cluster boundaries, so only the last key tile of a query cluster is partial.
+ *   q, k, v     device, [B, H, N, d] SA_BF16, in the permuted orders (queries by the query
+ *               clusters, keys and values by the key clusters).
+ *   q_offsets   device, [B, H, Cq + 1] int32; k_offsets device, [B, H, Ck + 1] int32 (ascending,
+ *               from 0 to N; not checked).
+ *   mask        device, [B, H, Cq, Ck] uint8.
+ *   o           device out, [B, H, N, d] bf16 in the permuted query order; lse device out or
+ *               NULL, [B, H, N] float32.
+ *   workspace   device scratch of at least sparse_attn_cluster_fwd_workspace_size() bytes,
+ *               256-byte aligned; overwritten.
+ * d in {64, 128}, Bq in {64, 128}, 1 <= Cq, Ck <= min(N, SA_MAX_CLUSTERS).
+ */
+int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
+                            const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck, const uint8_t* mask,
+                            int Bq, double scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Host helper: the Top-k size for a fraction, as select_mask computes it (-1 if invalid). */
 int sparse_attn_topk_count(double k_frac, int nkb);
