@@ -329,6 +329,97 @@ def corrected_bench(args, sa, w, q, k, v, gen_s):
     }
 
 
+def svg2_bench(args, sa, w, q, k, v, gen_s):
+    """Semantic-aware permutation end to end: k-means of Q (Cq clusters) and K (Ck clusters),
+    centroid Top-p, permutation of Q / K / V, attention over the variable-size blocks and the
+    inverse permutation of O. Executed FLOPs are 4 d per kept (query, key) pair, counted exactly
+    from the clusters (no padding). ``--svg2-warm`` starts each step's k-means from the previous
+    step's centroids with one iteration (the centroid cache), otherwise every step starts from
+    evenly spaced tokens and runs ``--svg2-iters`` iterations."""
+    import numpy as np
+    import torch
+    B, H, N, d = q.shape
+    Cq, Ck, p = args.svg2_clusters
+    iters = 1 if args.svg2_warm else args.svg2_iters
+    cache = {}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        kq = sa.kmeans(q, Cq, iters, init=cache.get("q"))
+        kk = sa.kmeans(k, Ck, iters, init=cache.get("k"))
+        if args.svg2_warm:
+            cache["q"], cache["k"] = kq["centroids"], kk["centroids"]
+        if ev is not None:
+            ev[1].record()
+        mask = sa.cluster_select(kq["centroids"], kk["centroids"], kk["offsets"], p)
+        qp, kp, vp = sa.permute_rows(q, kq["perm"]), sa.permute_rows(k, kk["perm"]), sa.permute_rows(v, kk["perm"])
+        if ev is not None:
+            ev[2].record()
+        op = sa.cluster_fwd(qp, kp, vp, kq["offsets"], kk["offsets"], mask, w.bq)
+        if ev is not None:
+            ev[3].record()
+        o = sa.permute_rows(op, kq["perm"], inverse=True)
+        if ev is not None:
+            ev[4].record()
+        return o, kq, kk, mask
+
+    if args.svg2_warm:  # fill the cache with a converged cold start, outside the timed region
+        kq0, kk0 = sa.kmeans(q, Cq, args.svg2_iters), sa.kmeans(k, Ck, args.svg2_iters)
+        cache["q"], cache["k"] = kq0["centroids"], kk0["centroids"]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(args.steps):
+        o, kq, kk, mask = step(evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs]).mean(axis=0)
+    nq = np.diff(kq["offsets"].cpu().numpy().astype(np.int64), axis=-1)
+    nk = np.diff(kk["offsets"].cpu().numpy().astype(np.int64), axis=-1)
+    m = mask.cpu().numpy().astype(np.int64)
+    pairs = float(np.einsum("bhi,bhij,bhj->", nq, m, nk))
+    kept_keys = np.einsum("bhij,bhj->bhi", m, nk)
+    key_tiles = np.ceil(kept_keys / 64.0)
+    q_tiles = np.ceil(nq / w.bq)
+    tile_flops = 4.0 * d * w.bq * 64 * float((q_tiles * key_tiles).sum())
+    flops = 4.0 * d * pairs
+    attn_tf = flops / (per[2] * 1e-3) / 1e12
+    # sampled quality: 8 positional query blocks per head, exact rows from the dense forward
+    nqb, nkb = -(-N // w.bq), -(-N // w.bk)
+    held = sorted({int((j + 0.25) * nqb / 8) for j in range(8)})
+    m_ex = torch.zeros((B, H, nqb, nkb), dtype=torch.uint8, device=q.device)
+    m_ex[:, :, held] = 1
+    o_ex = sa.fwd(q, k, v, m_ex, w.bq, w.bk)
+    rows = torch.cat([torch.arange(i * w.bq, min(N, (i + 1) * w.bq)) for i in held]).to(q.device)
+    ex, sp = o_ex[:, :, rows].float(), o[:, :, rows].float()
+    return {
+        "metric": "semantic-aware permutation attention TFLOP/s (executed, whole step)",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: k-means permutation, {Cq} query / {Ck} key clusters, p = {p}, "
+                               f"{'warm start, 1 iteration' if args.svg2_warm else f'{iters} iterations from evenly spaced tokens'}",
+                   "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq, "query_clusters": Cq,
+                   "key_clusters": Ck, "p": p, "kmeans_iters": iters, "kept_pair_density": round(pairs / (B * H * N * N), 5),
+                   "executed_tflop_per_step": round(flops / 1e12, 4), "tile_tflop_per_step": round(tile_flops / 1e12, 4),
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_call": {"kmeans_q+k": round(float(per[0]), 4), "cluster_select+permute": round(float(per[1]), 4),
+                        "cluster_fwd": round(float(per[2]), 4), "inverse_permute": round(float(per[3]), 4)},
+        "cluster_fwd_tflops": round(attn_tf, 2),
+        "sampled_rel_l2_error_vs_dense": round(float((sp - ex).norm() / ex.norm()), 5),
+        "roofline": {"kernel": "attn_var_kernel<128, 128>", "bound": "mfma", "achieved": round(attn_tf, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "input_generation_s": round(gen_s, 1),
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +442,14 @@ def main(argv=None):
     ap.add_argument("--correct", type=int, default=0, metavar="PROBES",
                     help="time the hot path followed by the probe-fitted residual correction with PROBES probe "
                          "query blocks per head (ridge 1e-3), and report held-out error before and after")
+    ap.add_argument("--svg2", action="store_true",
+                    help="time the semantic-aware permutation path (k-means clusters, centroid Top-p, attention "
+                         "over variable-size blocks) instead of the block-mask path")
+    ap.add_argument("--svg2-clusters", type=float, nargs=3, default=(128, 256, 0.9), metavar=("CQ", "CK", "P"),
+                    help="query clusters, key clusters and Top-p threshold of --svg2 (default 128 256 0.9)")
+    ap.add_argument("--svg2-iters", type=int, default=3, help="k-means iterations of --svg2 (default 3)")
+    ap.add_argument("--svg2-warm", action="store_true",
+                    help="with --svg2: start every step from the previous step's centroids, one iteration")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -398,6 +497,10 @@ def main(argv=None):
         return 0
     if args.correct:
         print(json.dumps(corrected_bench(args, sa, w, q, k, v, gen_s)), flush=True)
+        return 0
+    if args.svg2:
+        args.svg2_clusters = (int(args.svg2_clusters[0]), int(args.svg2_clusters[1]), float(args.svg2_clusters[2]))
+        print(json.dumps(svg2_bench(args, sa, w, q, k, v, gen_s)), flush=True)
         return 0
 
     def step(ev=None):

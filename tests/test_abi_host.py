@@ -229,3 +229,82 @@ def test_probe_workspace_size():
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, probes) == want
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, 96, bq, probes) == 0
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, 0) == 0
+
+
+def _km(**kw):
+    ws = _lib.lib().sparse_attn_kmeans_workspace_size(1, 2, 1000, 64, 16)
+    a = dict(x=P, dtype=0, B=1, H=2, N=1000, d=64, C=16, iters=2, init=None, cen=P, labels=P, perm=P, off=P, ws=P,
+             ws_bytes=ws, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_kmeans(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(cen=None), -1), (dict(perm=None), -1), (dict(ws=None), -1), (dict(ws_bytes=64), -1),
+    (dict(ws=P + 16), -1), (dict(x=P_ODD), -1), (dict(C=0), -1), (dict(C=1001), -1), (dict(iters=0), -1),
+    (dict(dtype=1), -2), (dict(d=96), -2),
+])
+def test_kmeans_rejects(kw, code):
+    assert _km(**kw) == code
+
+
+def test_kmeans_rejects_too_many_clusters():
+    assert _km(N=5000, C=1025, ws_bytes=1 << 30) == -2
+
+
+def _csel(**kw):
+    a = dict(cq=P, ck=P, off=P, B=1, H=2, Cq=8, Ck=40, d=64, scale=0.125, p=0.9, probs=None, mask=P, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_cluster_select(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), -1), (dict(off=None), -1), (dict(mask=None), -1), (dict(Cq=0), -1), (dict(p=1.5), -1),
+    (dict(p=-0.1), -1), (dict(scale=0.0), -1), (dict(d=32), -2), (dict(Ck=1025), -2),
+])
+def test_cluster_select_rejects(kw, code):
+    assert _csel(**kw) == code
+
+
+def _perm(**kw):
+    a = dict(x=P, dtype=0, B=1, H=2, N=1000, d=64, perm=P + 4096, inverse=0, out=P + 8192, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_permute_rows(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(perm=None), -1), (dict(out=P), -1), (dict(out=P_ODD), -1), (dict(d=96), -2),
+    (dict(dtype=4), -2),
+])
+def test_permute_rows_rejects(kw, code):
+    assert _perm(**kw) == code
+
+
+def _cfwd(**kw):
+    ws = _lib.lib().sparse_attn_cluster_fwd_workspace_size(1, 2, 1000, 8, 40, 128)
+    a = dict(q=P, k=P, v=P, dtype=0, B=1, H=2, N=1000, d=64, qo=P, Cq=8, ko=P, Ck=40, mask=P, Bq=128, scale=0.125, o=P,
+             lse=None, ws=P, ws_bytes=ws, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_cluster_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qo=None), -1), (dict(mask=None), -1), (dict(ws=None), -1), (dict(ws_bytes=64), -1), (dict(o=None), -1),
+    (dict(Cq=0), -1), (dict(Ck=1001), -1), (dict(dtype=1), -2), (dict(Bq=32), -2), (dict(scale=-1.0), -1),
+])
+def test_cluster_fwd_rejects(kw, code):
+    assert _cfwd(**kw) == code
+
+
+def test_cluster_workspace_sizes():
+    lib = _lib.lib()
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    bh, n, d, c = 2, 1000, 64, 40
+    cp, nch = 64, 4
+    assert lib.sparse_attn_kmeans_workspace_size(1, 2, n, d, c) == \
+        2 * al(bh * cp * d * 2) + al(bh * cp * 4) + al(bh * n * 4) + al(bh * nch * c * 4)
+    mt = 8 + 8
+    assert lib.sparse_attn_cluster_fwd_workspace_size(1, 2, n, 8, 40, 128) == \
+        al(bh * mt * 16) + al(bh * 4) + al(bh * 8 * 40 * 4) + al(bh * 8 * 4)
+    assert lib.sparse_attn_kmeans_workspace_size(1, 2, n, 96, c) == 0
+    assert lib.sparse_attn_cluster_fwd_workspace_size(1, 2, n, 8, 40, 96) == 0
