@@ -392,7 +392,8 @@ def svg2_bench(args, sa, w, q, k, v, gen_s):
     attn_tf = flops / (per[2] * 1e-3) / 1e12
     # sampled quality: 8 positional query blocks per head, exact rows from the dense forward
     nqb, nkb = -(-N // w.bq), -(-N // w.bk)
-    held = sorted({int((j + 0.25) * nqb / 8) for j in range(8)})
+    full = nqb if N % w.bq == 0 else max(nqb - 1, 1)
+    held = sorted({min(full - 1, int((j + 0.25) * full / 8)) for j in range(8)})  # the --correct blocks
     m_ex = torch.zeros((B, H, nqb, nkb), dtype=torch.uint8, device=q.device)
     m_ex[:, :, held] = 1
     o_ex = sa.fwd(q, k, v, m_ex, w.bq, w.bk)
