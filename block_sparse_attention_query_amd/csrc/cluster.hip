@@ -56,22 +56,26 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 
 // Operands of the assignment for centroid c of head bh: high and low bf16 parts (padded rows
 // past C are zero) and the fp32 squared norm (+inf for padded rows, which are never chosen).
-template <int D>
+// Called by every thread of the workgroup; threads 0 .. D - 1 hold channel vch.
+template <int D, int NT>
 __device__ __forceinline__ void km_write_operands(const float vch, int bh, int c, int C, int CP, __bf16* chi,
                                                   __bf16* clo, float* cn, float* red) {
   const int ch = threadIdx.x;
-  const __bf16 hi = (__bf16)vch;
-  const __bf16 lo = (__bf16)(vch - (float)hi);
-  chi[((size_t)bh * CP + c) * D + ch] = hi;
-  clo[((size_t)bh * CP + c) * D + ch] = lo;
-  float sq = vch * vch;
+  float sq = 0.f;
+  if (ch < D) {
+    const __bf16 hi = (__bf16)vch;
+    const __bf16 lo = (__bf16)(vch - (float)hi);
+    chi[((size_t)bh * CP + c) * D + ch] = hi;
+    clo[((size_t)bh * CP + c) * D + ch] = lo;
+    sq = vch * vch;
+  }
   for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
   if ((ch & 63) == 0) red[ch >> 6] = sq;
   __syncthreads();
   if (ch == 0) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) s += red[w];
+    for (int w = 0; w < NT / 64; ++w) s += red[w];
     cn[(size_t)bh * CP + c] = c < C ? s : INFINITY;
   }
 }
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(D) void km_init_kernel(const uint16_t* __restrict__
     }
     cen[((size_t)bh * C + c) * D + ch] = v;
   }
-  km_write_operands<D>(v, bh, c, C, CP, chi, clo, cn, red);
+  km_write_operands<D, D>(v, bh, c, C, CP, chi, clo, cn, red);
 }
 
 // Grid (BH, ceil(N / 256)), 4 waves of 64 tokens (two sets of 32). Centroids stream through LDS
@@ -236,40 +240,53 @@ __global__ __launch_bounds__(KM_CH) void km_scatter_kernel(const int32_t* __rest
   perm[(size_t)bh * N + pos] = t;
 }
 
-// Grid (BH, CP), D threads: centroid c = the float64 mean of its tokens, summed in permuted order
-// (an empty cluster keeps its centroid), then its MFMA operands.
+// Grid (BH, CP), 256 threads: centroid c = the float64 mean of its tokens (an empty cluster keeps
+// its centroid), then its MFMA operands. Thread (g, ch), g < 256 / D, sums channel ch over the
+// members o0 + g, o0 + g + 256 / D, ... of the cluster's run of the permuted order, eight loads in
+// flight; the partial sums are added in the order of g, so the result is deterministic.
 template <int D>
-__global__ __launch_bounds__(D) void km_update_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                      const int32_t* __restrict__ offsets, int N, int C, int CP,
-                                                      float* __restrict__ cen, __bf16* __restrict__ chi,
-                                                      __bf16* __restrict__ clo, float* __restrict__ cn) {
-  __shared__ float red[D / 64];
-  const int bh = blockIdx.x, c = blockIdx.y, ch = threadIdx.x;
-  float v = 0.f;
+__global__ __launch_bounds__(256) void km_update_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                                                        const int32_t* __restrict__ offsets, int N, int C, int CP,
+                                                        float* __restrict__ cen, __bf16* __restrict__ chi,
+                                                        __bf16* __restrict__ clo, float* __restrict__ cn) {
+  constexpr int G = 256 / D;
+  __shared__ double part[G][D];
+  __shared__ float red[4];
+  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int g = tid / D, ch = tid % D;
+  int o0 = 0, o1 = 0;
   if (c < C) {
-    const int o0 = offsets[(size_t)bh * (C + 1) + c], o1 = offsets[(size_t)bh * (C + 1) + c + 1];
+    o0 = offsets[(size_t)bh * (C + 1) + c];
+    o1 = offsets[(size_t)bh * (C + 1) + c + 1];
+  }
+  const uint16_t* xh = x + (size_t)bh * N * D + ch;
+  const int32_t* pp = perm + (size_t)bh * N;
+  double acc = 0.0;
+  int m = o0 + g;
+  for (; m + 7 * G < o1; m += 8 * G) {
+    uint32_t b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = xh[(size_t)pp[m + u * G] * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)__uint_as_float(b[u] << 16);
+  }
+  for (; m < o1; m += G) acc += (double)__uint_as_float((uint32_t)xh[(size_t)pp[m] * D] << 16);
+  part[g][ch] = acc;
+  __syncthreads();
+  float v = 0.f;
+  if (tid < D && c < C) {
     float* cp = cen + ((size_t)bh * C + c) * D + ch;
     if (o1 > o0) {
-      const uint16_t* xh = x + (size_t)bh * N * D + ch;
-      const int32_t* pp = perm + (size_t)bh * N;
-      double acc = 0.0;
-      int m = o0;
-      for (; m + 4 <= o1; m += 4) {  // four independent loads in flight, summed in order
-        const int t0 = pp[m], t1 = pp[m + 1], t2 = pp[m + 2], t3 = pp[m + 3];
-        const uint32_t a = xh[(size_t)t0 * D], b = xh[(size_t)t1 * D], e = xh[(size_t)t2 * D], f = xh[(size_t)t3 * D];
-        acc += (double)__uint_as_float(a << 16);
-        acc += (double)__uint_as_float(b << 16);
-        acc += (double)__uint_as_float(e << 16);
-        acc += (double)__uint_as_float(f << 16);
-      }
-      for (; m < o1; ++m) acc += (double)__uint_as_float((uint32_t)xh[(size_t)pp[m] * D] << 16);
-      v = (float)(acc / (double)(o1 - o0));
+      double s = part[0][ch];
+#pragma unroll
+      for (int h = 1; h < G; ++h) s += part[h][ch];
+      v = (float)(s / (double)(o1 - o0));
       *cp = v;
     } else {
       v = *cp;
     }
   }
-  km_write_operands<D>(v, bh, c, C, CP, chi, clo, cn, red);
+  km_write_operands<D, 256>(v, bh, c, C, CP, chi, clo, cn, red);
 }
 
 // ---------------------------------------------------------------- centroid Top-p
@@ -693,7 +710,7 @@ hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, 
     hipLaunchKernelGGL(km_scan_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, hist, C, nch, offsets);       \
     hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, rank,  \
                        hist, offsets, N, C, nch, perm);                                                            \
-    hipLaunchKernelGGL((km_update_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(D_), 0, stream, xs, perm,     \
+    hipLaunchKernelGGL((km_update_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(256), 0, stream, xs, perm,     \
                        offsets, N, C, CP, cen, chi, clo, cn);                                                      \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                                           \
   }
