@@ -309,7 +309,7 @@ def corrected_bench(args, sa, w, q, k, v, gen_s):
         "metric": "sparse attention fwd + probe-fitted correction TFLOP/s (executed)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic" + (", smooth values" if args.smooth_v else ""),
         "config": {"workload": f"{w.name}: hybrid mask, then {P} probe blocks per head", "batch": B, "heads": H,
                    "tokens": N, "head_dim": d, "bq": w.bq, "bk": w.bk, "k_frac": w.k_frac, "p": w.p,
                    "probes": P, "ridge": ridge, "kept_block_density": round(float(mask_cpu.mean()), 5),
@@ -403,7 +403,7 @@ def svg2_bench(args, sa, w, q, k, v, gen_s):
         "metric": "semantic-aware permutation attention TFLOP/s (executed, whole step)",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic" + (", smooth values" if args.smooth_v else ""),
         "config": {"workload": f"{w.name}: k-means permutation, {Cq} query / {Ck} key clusters, p = {p}, "
                                f"{'warm start, 1 iteration' if args.svg2_warm else f'{iters} iterations from evenly spaced tokens'}",
                    "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq, "query_clusters": Cq,
@@ -451,6 +451,9 @@ def main(argv=None):
     ap.add_argument("--svg2-iters", type=int, default=3, help="k-means iterations of --svg2 (default 3)")
     ap.add_argument("--svg2-warm", action="store_true",
                     help="with --svg2: start every step from the previous step's centroids, one iteration")
+    ap.add_argument("--smooth-v", action="store_true",
+                    help="spatially smooth values (a second standardised Gaussian field plus noise) instead of "
+                         "i.i.d. ones; for the quality figures of --correct and --svg2")
     ap.add_argument("--sweep-out", default=None,
                     help="also time the attention call on the density sweep and write JSON lines here")
     args = ap.parse_args(argv)
@@ -477,7 +480,7 @@ def main(argv=None):
 
     w = WORKLOADS[args.workload]
     t0 = time.perf_counter()
-    x = make_inputs(w)
+    x = make_inputs(w, smooth_v=args.smooth_v)
     gen_s = time.perf_counter() - t0
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in (x["q"], x["k"], x["v"]))

@@ -17,6 +17,14 @@ the draws taken in this order:
 4. Cast to the storage type with round-to-nearest-even (torch ``.to``).
 
 Heads are generated independently, so any subset of heads reproduces the same values.
+
+Structured values (``make_inputs(..., smooth_v=True)``, used only for the quality figures of the
+correction and permutation paths): ``V`` is instead a second field ``G``, drawn from its own
+generator ``numpy.random.default_rng([seed, b, h, 1])`` and smoothed and standardised like ``F``
+(independent of it), plus ``0.3 * N(0, 1)`` from the same generator. Q, K and the sinks are
+unchanged. In a video DiT, V is a projection of the same spatially smooth hidden states as Q and
+K, so nearby tokens carry similar values; the i.i.d. default is the harder case for any method
+that reconstructs values from neighbours.
 """
 
 from __future__ import annotations
@@ -60,7 +68,7 @@ def _blur(f: np.ndarray, sigma: tuple) -> np.ndarray:
     return f
 
 
-def _head(w: Workload, b: int, h: int):
+def _head(w: Workload, b: int, h: int, smooth_v: bool = False):
     rng = np.random.default_rng([w.seed, b, h])
     t, y, x = w.grid
     n, d = w.tokens, w.head_dim
@@ -70,6 +78,11 @@ def _head(w: Workload, b: int, h: int):
     q = f + np.float32(w.noise_std) * rng.standard_normal((n, d)).astype(np.float32)
     k = f + np.float32(w.noise_std) * rng.standard_normal((n, d)).astype(np.float32)
     v = rng.standard_normal((n, d)).astype(np.float32)
+    if smooth_v:
+        rv = np.random.default_rng([w.seed, b, h, 1])
+        g = _blur(rv.standard_normal((t, y, x, d)).astype(np.float32), w.sigma).reshape(n, d)
+        g = (g - g.mean(axis=0, keepdims=True)) / g.std(axis=0, keepdims=True)
+        v = g + np.float32(w.noise_std) * rv.standard_normal((n, d)).astype(np.float32)
     sinks = []
     if w.kind == "locality_sink":
         s = int(rng.integers(n))
@@ -89,7 +102,7 @@ def _head(w: Workload, b: int, h: int):
     return (torch.from_numpy(q).to(dt), torch.from_numpy(k).to(dt), torch.from_numpy(v).to(dt), sinks)
 
 
-def make_inputs(w: Workload, heads=None, threads: int | None = None):
+def make_inputs(w: Workload, heads=None, threads: int | None = None, smooth_v: bool = False):
     """Q, K, V as CPU tensors ``[B, len(heads), N, d]`` of the workload's storage type.
 
     Returns a dict with ``q``, ``k``, ``v``, ``heads`` (the head indices generated) and
@@ -99,7 +112,7 @@ def make_inputs(w: Workload, heads=None, threads: int | None = None):
     jobs = [(b, h) for b in range(w.batch) for h in heads]
     threads = threads or min(16, len(os.sched_getaffinity(0)), len(jobs))
     with ThreadPoolExecutor(max(1, threads)) as ex:
-        res = list(ex.map(lambda bh: _head(w, *bh), jobs))
+        res = list(ex.map(lambda bh: _head(w, *bh, smooth_v=smooth_v), jobs))
     dt = torch_dtype(w)
     shape = (w.batch, len(heads), w.tokens, w.head_dim)
     q = torch.empty(shape, dtype=dt)
