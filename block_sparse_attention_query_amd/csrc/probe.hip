@@ -14,6 +14,7 @@
 // Kernels: probe_partial (MFMA, the forward's tile layout), probe_combine, probe_gram (fp64 MFMA),
 // probe_chol and probe_subst (fp64) and probe_apply (bf16 MFMA, HBM-bound).
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_tiles.h"
 
@@ -25,31 +26,45 @@ __host__ __device__ inline int probe_block(int p, int P, int nqb, int N, int BQ)
   return min(full - 1, i);
 }
 
-// Number of key-block ranges of the probes' dense attention: about 1024 workgroups in all, with
-// at least 4 key blocks per range.
+// Number S of key-block ranges of the probes' dense attention. The BH P S workgroups run in
+// rounds of 512 (two per CU); S minimises rounds x key blocks per range (the smaller S on a tie),
+// with at most 24 ranges (each adds a partial output to write and merge) and at least 4 key
+// blocks per range.
 inline int probe_splits(int BH, int P, int nkb) {
   const long long units = (long long)BH * P;
-  const int want = (int)std::max(1LL, (1024 + units - 1) / units);
-  return std::max(1, std::min(want, nkb / 4));
+  const int smax = std::max(1, std::min(24, nkb / 4));
+  int best = 1;
+  long long best_cost = -1;
+  for (int S = 1; S <= smax; ++S) {
+    const long long cost = ((units * S + 511) / 512) * ((nkb + S - 1) / S);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
 }
 
 // ---------------------------------------------------------------- 2a. partial dense attention
 
 // One workgroup per (bh, range s, probe p), BQ / 32 waves of 32 queries, over key blocks
-// [s nkb / S, (s + 1) nkb / S). The S^T = K Q^T and O^T += V^T P^T products and the tile layout
-// are the forward kernel's; every key block of the range is kept. Writes, per query, the
-// unnormalised output sum_u 2^(c s_u - m) V_u (fp32), its reference m (log2 domain) and the
-// sum l of the same weights. Partial index: (bh S + s) P + p.
+// [s nkb / S, (s + 1) nkb / S). The S^T = K Q^T and O^T += V^T P^T products, the tile layout and
+// the two-stage software pipeline are the forward kernel's (step t computes the scores of block
+// t + 1 while P V of block t accumulates; K runs one block ahead of V in LDS); every key block of
+// the range is kept. Writes, per query, the unnormalised output sum_u 2^(c s_u - m) V_u (fp32),
+// its reference m (log2 domain) and the sum l of the same weights. Partial index: (bh S + s) P + p.
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                                   const void* __restrict__ v, int N, int nqb, int nkb,
                                                                   int P, int S, float c_log2, float* __restrict__ part_o,
                                                                   float* __restrict__ part_ml) {
   using C = DCfg<D, BQ>;
-  __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];
-  __shared__ __attribute__((aligned(1024))) char buf1_[2 * C::TILE];
-  lchar* const buf0 = (lchar*)buf0_;
-  lchar* const buf1 = (lchar*)buf1_;
+  __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
+  lchar* const kb0 = (lchar*)kbuf_;
+  lchar* const kb1 = kb0 + C::TILE;
+  lchar* const vb0 = (lchar*)vbuf_;
+  lchar* const vb1 = vb0 + C::TILE;
 
   // the P probes of one range run on one XCD and share its L2 for the key / value blocks
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
@@ -57,12 +72,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __
   const int s = (unit / P) % S;
   const int bh = unit / (P * S);
   const int qb = probe_block(p, P, nqb, N, BQ);
-  const int kb0 = (int)((long long)s * nkb / S), kb1 = (int)((long long)(s + 1) * nkb / S);
-  const int cnt = kb1 - kb0;
+  const int first = (int)((long long)s * nkb / S);
+  const int cnt = (int)((long long)(s + 1) * nkb / S) - first;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31;
   const int hf = lane >> 5;
+  auto blk = [&](int i) { return first + i; };
 
   const size_t head_off = (size_t)bh * N * D * 2;
   const char* qbase = static_cast<const char*>(q) + head_off;
@@ -71,9 +87,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __
   uint32_t doff[C::PER_WAVE];
   dma_offsets<D, BQ>(wave, lane, doff);
   if (cnt > 0) {
-    dma_tile<D, BQ>(kbase, kb0, N, wave, lane, doff, buf0);
-    dma_tile<D, BQ>(vbase, kb0, N, wave, lane, doff, buf0 + C::TILE);
+    dma_tile<D, BQ>(kbase, blk(0), N, wave, lane, doff, kb0);
+    dma_tile<D, BQ>(vbase, blk(0), N, wave, lane, doff, vb0);
   }
+  if (cnt > 1) dma_tile<D, BQ>(kbase, blk(1), N, wave, lane, doff, kb1);
   // Q^T fragments: query 32 wave + ln, channels 16 j + 8 hf .. + 7 (rows past N are zero)
   const int qrow = qb * BQ + wave * 32 + ln;
   const bool qvalid = qrow < N;
@@ -113,43 +130,39 @@ __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __
   float m_run = -INFINITY, l_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int t = 0; t < cnt; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block t is resident; every wave is done with block t - 1
-    if (t + 1 < cnt) {
-      lchar* nb = (t & 1) ? buf0 : buf1;
-      dma_tile<D, BQ>(kbase, kb0 + t + 1, N, wave, lane, doff, nb);
-      dma_tile<D, BQ>(vbase, kb0 + t + 1, N, wave, lane, doff, nb + C::TILE);
-    }
-    const lchar* kt = (t & 1) ? buf1 : buf0;
-    lchar* vt = ((t & 1) ? buf1 : buf0) + C::TILE;
-    const int kb = kb0 + t;
-    f32x16 s0, s1;
+  auto scores = [&](const lchar* kt, f32x16 (&sc)[2]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
+      sc[0][i] = 0.f;
+      sc[1][i] = 0.f;
     }
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
       const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[j]);
       const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[j] + 32 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], s1, 0, 0, 0);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], sc[1], 0, 0, 0);
     }
-    if (kb * BK + BK > N) {  // keys past N in the ragged last block
+  };
+  auto mask_tail = [&](f32x16 (&sc)[2], int kb) {  // keys past N in the ragged last block
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (key >= N) s0[i] = -INFINITY;
-        if (key + 32 >= N) s1[i] = -INFINITY;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (key >= N) sc[0][i] = -INFINITY;
+      if (key + 32 >= N) sc[1][i] = -INFINITY;
     }
-    float mx = -INFINITY;
+  };
+  auto block_max = [&](const f32x16 (&sc)[2]) {
+    float m4[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = partner32_max(mx) * c_log2;
-    if (__ballot(mx > m_run + 8.f)) {  // lazy rescale: weights stay below 2^8 between raises
+    for (int c = 0; c < 4; ++c) m4[c] = fmaxf(sc[0][c], sc[1][c]);
+#pragma unroll
+    for (int i = 4; i < 16; ++i) m4[i & 3] = fmaxf(fmaxf(m4[i & 3], sc[0][i]), sc[1][i]);
+    const float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    return partner32_max(mx) * c_log2;
+  };
+  auto raise_max = [&](float mx) {  // lazy rescale: weights stay below 2^8 between raises
+    if (__ballot(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -159,24 +172,27 @@ __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __
         for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
       m_run = m_new;
     }
+  };
+  auto accumulate = [&](const f32x16 (&sc)[2], lchar* vt) {
     bf16x8 pb[4];
-    float rs = 0.f;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       uint32_t w0[4], w1[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
-        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
+        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e + 1], c_log2, -m_run)));
+        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e + 1], c_log2, -m_run)));
+        rs[(e & 1) * 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs[(e & 1) * 2], false);
+        rs[(e & 1) * 2 + 1] =
+            __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs[(e & 1) * 2 + 1], false);
       }
       pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
       pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
     }
-    l_run += rs;
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -188,6 +204,57 @@ __global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __
         const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
       }
+  };
+
+  const bool ragged_last = cnt > 0 && (N % BK) != 0 && blk(cnt - 1) == nkb - 1;
+  // Step t. NEXT: 0 = no block t + 1 (last step), 1 = full block t + 1, 2 = ragged block t + 1.
+  // kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1).
+  auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
+                  auto next_tag) {
+    constexpr int NEXT = decltype(next_tag)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
+    if constexpr (NEXT != 0) {
+      scores(kn, sn);
+      if constexpr (NEXT == 2) mask_tail(sn, blk(t + 1));
+    }
+    if (t + 2 < cnt) dma_tile<D, BQ>(kbase, blk(t + 2), N, wave, lane, doff, kf);
+    if (t + 1 < cnt) dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, vf);
+    accumulate(sc, vc);
+    if constexpr (NEXT != 0) raise_max(block_max(sn));
+  };
+
+  using last = std::integral_constant<int, 0>;
+  using full = std::integral_constant<int, 1>;
+  using rag = std::integral_constant<int, 2>;
+  if (cnt > 0) {
+    f32x16 sa[2], sb[2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    scores(kb0, sa);
+    if (ragged_last && cnt == 1) mask_tail(sa, blk(0));
+    raise_max(block_max(sa));
+    const int nfull = ragged_last ? cnt - 2 : cnt - 1;
+    int t = 0;
+    for (; t + 1 < nfull; t += 2) {
+      step(t, sa, sb, kb1, vb0, kb0, vb1, full{});
+      step(t + 1, sb, sa, kb0, vb1, kb1, vb0, full{});
+    }
+    if (t < nfull) {
+      step(t, sa, sb, kb1, vb0, kb0, vb1, full{});
+      ++t;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+    }
+    const bool odd = (t & 1) != 0;
+    if (t + 1 < cnt) {
+      step(t, sa, sb, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1, rag{});
+      ++t;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+    }
+    const bool odd2 = (t & 1) != 0;
+    step(t, sa, sb, odd2 ? kb0 : kb1, odd2 ? vb1 : vb0, odd2 ? kb1 : kb0, odd2 ? vb0 : vb1, last{});
   }
   // element i of oacc[r] is channel 32 r + 8 (i / 4) + 4 hf + i % 4 of query 32 wave + ln
   const size_t qo = (size_t)unit * BQ + wave * 32 + ln;

@@ -212,15 +212,17 @@ def test_probe_correct_rejects(kw, code):
 
 
 def test_probe_workspace_size():
-    """Partial outputs of S key-block ranges (about 1024 workgroups in all, at least 4 key blocks
-    per range), the exact probe rows, [G | C] in float64, the factor (rows padded to blocks of 8
-    plus the n reciprocals of its diagonal, an even count of float64), A, A^T in bf16 and the bias
-    row."""
+    """Partial outputs of S key-block ranges (S minimises rounds of 512 workgroups times key
+    blocks per range, at most 24 ranges, at least 4 key blocks per range), the exact probe rows,
+    [G | C] in float64, the factor (rows padded to blocks of 8 plus the n reciprocals of its
+    diagonal, an even count of float64), A, A^T in bf16 and the bias row."""
     lib = _lib.lib()
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     bh, n, d, bq, probes = 2, 1000, 128, 128, 3
     nkb = 16
-    s = max(1, min(-(-1024 // (bh * probes)), nkb // 4))
+    smax = max(1, min(24, nkb // 4))
+    costs = [(-(-(bh * probes * S) // 512)) * (-(-nkb // S)) for S in range(1, smax + 1)]
+    s = 1 + costs.index(min(costs))
     units = bh * probes * s
     m = d + 1
     fac = (m * (-(-m // 8) * 8) + m + 1) // 2 * 2
