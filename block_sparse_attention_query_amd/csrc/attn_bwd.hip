@@ -14,24 +14,34 @@ namespace sa {
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
 
+// D = rowsum(dO * O) and LSE * log2(e) for every query of the padded query blocks (NP per head):
+// rows past N get D = 0 and LSE = +inf, so that their P and dS vanish without a mask.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const char* __restrict__ dout, const char* __restrict__ o,
-                                                        float* __restrict__ delta, long long rows) {
+                                                        const float* __restrict__ lse, float* __restrict__ deltap,
+                                                        float* __restrict__ lse2p, int N, int NP, long long rows_p) {
   constexpr int VPR = D / 8;  // 16-byte chunks per bf16 row; VPR lanes reduce one row
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long r = e / VPR;
   const int c = (int)(e % VPR);
+  const long long bh = r / NP;
+  const int qi = (int)(r - bh * NP);
+  const bool valid = r < rows_p && qi < N;
+  const size_t row = (size_t)bh * N + qi;
   float acc = 0.f;
-  if (r < rows) {
-    const uint4 a = *reinterpret_cast<const uint4*>(dout + (size_t)r * D * 2 + c * 16);
-    const uint4 b = *reinterpret_cast<const uint4*>(o + (size_t)r * D * 2 + c * 16);
+  if (valid) {
+    const uint4 a = *reinterpret_cast<const uint4*>(dout + row * D * 2 + c * 16);
+    const uint4 b = *reinterpret_cast<const uint4*>(o + row * D * 2 + c * 16);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc += bf16_lo(wa[i]) * bf16_lo(wb[i]) + bf16_hi(wa[i]) * bf16_hi(wb[i]);
   }
 #pragma unroll
   for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (r < rows && c == 0) delta[r] = acc;
+  if (r < rows_p && c == 0) {
+    deltap[r] = acc;
+    lse2p[r] = valid ? lse[row] * 1.4426950408889634f : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------- mask columns
@@ -78,30 +88,6 @@ __device__ __forceinline__ bf16x8 tr_operand(const lchar* tile, int row0, int co
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// bf16 fragment of 8 consecutive elements of row `row`, logical 16-byte chunk `chunk`, from a
-// swizzled [row][col] tile (the layout the DMA helpers write).
-template <int ROWB, int SWZD>
-__device__ __forceinline__ bf16x8 row_operand(const lchar* tile, int row, int chunk) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-      tile + row * ROWB + ((chunk ^ kv_swz<SWZD>(row)) << 4));
-}
-
-// DMA of `rows` consecutive token rows (from row0; rows past N are clamped to N - 1) of a
-// [N][D] bf16 tensor into a swizzled LDS tile, by the NW waves of the workgroup.
-template <int D, int NW>
-__device__ __forceinline__ void dma_rows(const char* __restrict__ base, int row0, int rows, int N, int wave,
-                                         int lane, lchar* dst) {
-  constexpr int ROWB = 2 * D;
-  const int instr = rows * ROWB / 1024;
-  for (int m = wave; m < instr; m += NW) {
-    const int byte = m * 1024 + lane * 16;
-    const int row = byte / ROWB;
-    const int chunk = ((byte % ROWB) >> 4) ^ kv_swz<D>(row);
-    const int src = min(row0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(base + ((size_t)src * D + chunk * 8) * 2, dst + m * 1024, 16, 0, 0);
-  }
-}
-
 // ---------------------------------------------------------------- dQ
 
 // One workgroup per (b, h, query block), BQ / 32 waves of 32 queries, walking the kept list:
@@ -111,7 +97,7 @@ __device__ __forceinline__ void dma_rows(const char* __restrict__ base, int row0
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, const void* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ kidx,
+    const float* __restrict__ lse2p, const float* __restrict__ deltap, const int32_t* __restrict__ kidx,
     const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float scale, float c_log2, void* __restrict__ dq) {
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];  // [K | V], even blocks
@@ -152,8 +138,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(qbase + off) : make_uint4(0, 0, 0, 0));
     gf[s] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(gbase + off) : make_uint4(0, 0, 0, 0));
   }
-  const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * 1.4426950408889634f : INFINITY;
-  const float dlt = qvalid ? delta[(size_t)bh * N + qrow] : 0.f;
+  const float lse2 = lse2p[(size_t)bh * nqb * BQ + qrow];  // +inf past N
+  const float dlt = deltap[(size_t)bh * nqb * BQ + qrow];
 
   int koff[D / 16];
   {
@@ -252,45 +238,60 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_kernel(
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, int BQ>
-struct BCfg {
-  static constexpr int NW = BQ / 32;
+// Launch geometry of the dK / dV kernel: one workgroup of two waves per (b, h, key block j);
+// wave w owns keys 32 w .. 32 w + 31 of the block. The query side streams through LDS in steps
+// of 64 queries (one 64-row Q tile, one dO tile, their 64 LSE and 64 D values), double buffered.
+template <int D>
+struct KVCfg {
+  static constexpr int NW = 2;
   static constexpr int NT = NW * 64;
-  static constexpr int ROWB = 2 * D;              // bytes per token row of K, V, Q, dO tiles
-  static constexpr int KT = BK * ROWB;            // K or V tile
-  static constexpr int QT = BQ * ROWB;            // Q or dO tile
-  static constexpr int PROWB = 2 * BK;            // bytes per query row of the P^T / dS^T tiles
-  static constexpr int PT = BQ * PROWB;
-  static constexpr int OFF_V = KT, OFF_Q = 2 * KT, OFF_G = 2 * KT + QT, OFF_P = 2 * KT + 2 * QT,
-                       OFF_S = 2 * KT + 2 * QT + PT;
-  static constexpr int LDS = 2 * KT + 2 * QT + 2 * PT;
-  static constexpr int TILES = 2 * (D / 32);      // 32 x 32 output tiles of dK (and of dV)
-  static constexpr int TPW = TILES / NW;          // per wave
-  static constexpr int OROW = D * 2 + 16;
-  static_assert(TILES % NW == 0, "output tiles must split evenly over the waves");
-  static_assert(BK * OROW <= LDS, "output staging must fit");
+  static constexpr int ROWB = 2 * D;         // bytes per token row
+  static constexpr int TILE = 64 * ROWB;     // 64 rows of Q or of dO
+  static constexpr int OFF_G = TILE;         // dO tile
+  static constexpr int OFF_L = 2 * TILE;     // 64 floats: LSE * log2(e) (+inf on padded rows)
+  static constexpr int OFF_D = 2 * TILE + 256;  // 64 floats: D (0 on padded rows)
+  static constexpr int BUF = 2 * TILE + 512;
+  static constexpr int LDS = 2 * BUF;
+  static constexpr int OROW = D * 2 + 16;    // bytes per staged output row
+  static_assert(64 * OROW <= LDS, "output staging must fit");
 };
 
-// One workgroup per (b, h, key block j), walking the query blocks that keep j. Per query block:
-//   phase A, wave w on queries 32 w .. 32 w + 31: S^T = K_j Q^T and dP^T = V_j dO^T, then
-//     P^T = exp(S^T - LSE) and dS^T = P^T * (dP^T - D) * scale, written to LDS as [query][key];
-//   phase B, wave w on its output tiles: dV_j += P^T dO and dK_j += dS^T Q, every operand by
-//     transpose reads (the K dimension is the query, the rows of all four tiles).
+// Copies of the 64-row tile sb (token rows 64 sb .. + 63, clamped to N - 1) of a [N][D] bf16
+// tensor into a swizzled LDS tile by the two waves: instruction u of wave w fills the 1 KiB
+// stretch m = w PW + u; lane i fills its bytes 16 i .. + 15, i.e. row (1024 m + 16 i) / ROWB and
+// swizzled chunk slot ((1024 m + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
+template <int D>
+__device__ __forceinline__ void kv_dma(const char* __restrict__ base, int sb, int N, int wave, int lane, lchar* dst) {
+  constexpr int ROWB = 2 * D, PW = 64 * ROWB / 1024 / 2;
+#pragma unroll
+  for (int u = 0; u < PW; ++u) {
+    const int m = wave * PW + u;
+    const int byte = m * 1024 + lane * 16;
+    const int row = byte / ROWB;
+    const int chunk = ((byte % ROWB) >> 4) ^ kv_swz<D>(row);
+    const int src = min(sb * 64 + row, N - 1);
+    __builtin_amdgcn_global_load_lds(base + (size_t)src * ROWB + chunk * 16, dst + m * 1024, 16, 0, 0);
+  }
+}
+
+// One workgroup per (b, h, key block j), walking the 64-query steps of the query blocks that keep
+// j (the mask's column, ascending). The key side is resident in registers for the whole walk: K
+// and V rows of the wave's 32 keys are the B operands of S = Q K^T and dP = dO V^T (queries in
+// M, keys in N). The products' results leave each lane one key and 16 queries, which is the A
+// operand layout of dV += P^T dO and dK += dS^T Q (keys in M, queries in K) up to an order of the
+// queries inside each run of 16; the dO and Q operands of those products are transpose reads
+// whose row order matches it. So P and dS never leave registers and a step has one barrier: the
+// one that hands the next buffer to the copies.
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, const void* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ cidx,
+    const float* __restrict__ lse2p, const float* __restrict__ deltap, const int32_t* __restrict__ cidx,
     const int32_t* __restrict__ ccnt, int N, int nqb, int nkb, float scale, float c_log2, void* __restrict__ dk,
     void* __restrict__ dv) {
-  using C = BCfg<D, BQ>;
+  using C = KVCfg<D>;
+  constexpr int SPB = BQ / 64;  // 64-query steps per query block
   extern __shared__ __attribute__((aligned(1024))) char lds_[];
   lchar* const base = (lchar*)lds_;
-  lchar* const kt = base;
-  lchar* const vt = base + C::OFF_V;
-  lchar* const qt = base + C::OFF_Q;
-  lchar* const gt = base + C::OFF_G;
-  lchar* const pt = base + C::OFF_P;
-  lchar* const st = base + C::OFF_S;
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = tile / nkb;
@@ -301,117 +302,142 @@ __global__ __launch_bounds__(BQ * 2, 1) void attn_bwd_dkdv_kernel(
   const int hf = lane >> 5;
   const int cnt = min(max(ccnt[tile], 0), nqb);
   const int32_t* list = cidx + (size_t)tile * nqb;
+  const int NP = nqb * BQ;  // padded queries per head of the LSE and D arrays
+  // steps are the 64-query sub-blocks of the listed query blocks; when the last query block is
+  // ragged and its second half lies wholly past N, that half is not a step
+  int T = cnt * SPB;
+  if (SPB == 2 && cnt > 0 && min(max(list[cnt - 1], 0), nqb - 1) == nqb - 1 && (nqb - 1) * BQ + 64 >= N) T -= 1;
 
   const size_t head_off = (size_t)bh * N * D * 2;
   const char* qbase = static_cast<const char*>(q) + head_off;
-  const char* kbase = static_cast<const char*>(k) + head_off;
-  const char* vbase = static_cast<const char*>(v) + head_off;
   const char* gbase = static_cast<const char*>(dout) + head_off;
-  dma_rows<D, C::NW>(kbase, kb * BK, BK, N, wave, lane, kt);
-  dma_rows<D, C::NW>(vbase, kb * BK, BK, N, wave, lane, vt);
+  const float* l2base = lse2p + (size_t)bh * NP;
+  const float* dlbase = deltap + (size_t)bh * NP;
+  // copies of step t into buffer t & 1: both tiles, then wave 0 the LSE and wave 1 the D values
+#define SA_KV_ISSUE(T_)                                                                                  \
+  {                                                                                                      \
+    const int t_ = (T_);                                                                                 \
+    const int sb_ = min(max(list[t_ / SPB], 0), nqb - 1) * SPB + t_ % SPB;                               \
+    lchar* b_ = base + (t_ & 1) * C::BUF;                                                                \
+    kv_dma<D>(qbase, sb_, N, wave, lane, b_);                                                            \
+    kv_dma<D>(gbase, sb_, N, wave, lane, b_ + C::OFF_G);                                                 \
+    __builtin_amdgcn_global_load_lds((wave == 0 ? l2base : dlbase) + sb_ * 64 + lane, b_ + C::OFF_L + wave * 256, \
+                                     4, 0, 0);                                                           \
+  }
+  if (T > 0) SA_KV_ISSUE(0)
 
-  int koff[D / 16];
+  // K and V rows of key 32 w + ln, channels 16 s + 8 hf .. + 7: the B operands (keys past N are 0)
+  const int key = kb * BK + wave * 32 + ln;
+  const bool kvalid = key < N;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const size_t off = head_off + ((size_t)key * D + 16 * s + 8 * hf) * 2;
+    kf[s] = __builtin_bit_cast(bf16x8, kvalid ? *reinterpret_cast<const uint4*>(static_cast<const char*>(k) + off)
+                                              : make_uint4(0, 0, 0, 0));
+    vf[s] = __builtin_bit_cast(bf16x8, kvalid ? *reinterpret_cast<const uint4*>(static_cast<const char*>(v) + off)
+                                              : make_uint4(0, 0, 0, 0));
+  }
+  // A operands of S and dP: query row ln (+ 32 h) of the tile, logical chunk 2 s + hf
+  int roff[D / 16];
   {
     const int sw = kv_swz<D>(ln);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) koff[s] = ln * C::ROWB + (((2 * s + hf) ^ sw) << 4);
+    for (int s = 0; s < D / 16; ++s) roff[s] = ln * C::ROWB + (((2 * s + hf) ^ sw) << 4);
   }
-  f32x16 acc_v[C::TPW], acc_k[C::TPW];
+
+  f32x16 acc_k[D / 32], acc_v[D / 32];
 #pragma unroll
-  for (int a = 0; a < C::TPW; ++a)
+  for (int c = 0; c < D / 32; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc_v[a][i] = 0.f;
-      acc_k[a][i] = 0.f;
+      acc_k[c][i] = 0.f;
+      acc_v[c][i] = 0.f;
     }
 
-  for (int t = 0; t < cnt; ++t) {
-    const int ib = min(max(list[t], 0), nqb - 1);
-    __syncthreads();  // phase B of the previous query block is done with the Q, dO, P, dS tiles
-    dma_rows<D, C::NW>(qbase, ib * BQ, BQ, N, wave, lane, qt);
-    dma_rows<D, C::NW>(gbase, ib * BQ, BQ, N, wave, lane, gt);
-    const int qrow = ib * BQ + wave * 32 + ln;
-    const bool qvalid = qrow < N;
-    const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * 1.4426950408889634f : INFINITY;
-    const float dlt = qvalid ? delta[(size_t)bh * N + qrow] : 0.f;
+  for (int t = 0; t < T; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    __syncthreads();  // step t is resident; both waves are done with the buffer of step t - 1
+    if (t + 1 < T) SA_KV_ISSUE(t + 1)
+    const lchar* qt = base + (t & 1) * C::BUF;
+    const lchar* gt = qt + C::OFF_G;
 
-    // phase A: S^T and dP^T for this wave's 32 queries (rows 32 w + ln of the Q and dO tiles)
-    f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const int qo = koff[s] + wave * 32 * C::ROWB;  // the swizzle depends on the row's low bits only
-      const bf16x8 bq = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + qo);
-      const bf16x8 bg = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + qo);
-      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s]);
-      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s] + 32 * C::ROWB);
-      const bf16x8 c0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s]);
-      const bf16x8 c1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s] + 32 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq, s1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bg, p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, bg, p1, 0, 0, 0);
-    }
-    // P^T and dS^T to LDS, [query][key]: element i of tile h holds key 32 h + 8 (i / 4) + 4 hf + i % 4
-    // of query 32 w + ln, so each group of four is 8 contiguous bytes of the query's row
-    const int prow = wave * 32 + ln;
+    // S = Q K^T and dP = dO V^T for queries 32 h .. 32 h + 31 of the step: element i of lane
+    // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4
+    f32x16 sc[2], dp[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float pv[4], sv[4];
+      for (int i = 0; i < 16; ++i) {
+        sc[h][i] = 0.f;
+        dp[h][i] = 0.f;
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          const float sc = h == 0 ? s0[i] : s1[i];
-          const float dp = h == 0 ? p0[i] : p1[i];
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc, c_log2, -lse2));
-          sv[e] = pv[e] * (dp - dlt) * scale;
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 aq = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s] + 32 * h * C::ROWB);
+        const bf16x8 ag = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s] + 32 * h * C::ROWB);
+        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[s], sc[h], 0, 0, 0);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[s], dp[h], 0, 0, 0);
+      }
+
+    // P = exp(s - LSE) and dS = P (dP - D) scale, packed to bf16 as A operands: run u of half h
+    // takes elements 8 u .. 8 u + 7, i.e. queries 32 h + 16 u + 8 (e / 4) + 4 hf + e % 4
+    bf16x8 pa[2][2], sa[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        uint32_t wp[4], ws[4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int qi = 32 * h + 16 * u + 8 * g + 4 * hf;  // four consecutive queries
+          const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_L + qi * 4);
+          const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_D + qi * 4);
+          float pv[4], sv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 8 * u + 4 * g + e;
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[h][i], c_log2, -lv[e]));
+            sv[e] = pv[e] * (dp[h][i] - dv4[e]) * scale;
+          }
+          wp[2 * g] = pack_bf16(pv[0], pv[1]);
+          wp[2 * g + 1] = pack_bf16(pv[2], pv[3]);
+          ws[2 * g] = pack_bf16(sv[0], sv[1]);
+          ws[2 * g + 1] = pack_bf16(sv[2], sv[3]);
         }
-        const int chunk = 4 * h + g;  // 16-byte chunk of keys 32 h + 8 g .. + 7; this lane half's 8 bytes
-        const int off = prow * C::PROWB + ((chunk ^ kv_swz<BK>(prow)) << 4) + hf * 8;
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(pt + off) =
-            (u32x2){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
-        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(st + off) =
-            (u32x2){pack_bf16(sv[0], sv[1]), pack_bf16(sv[2], sv[3])};
+        pa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+        sa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
       }
-    __syncthreads();
 
-    // phase B: dV += P^T dO and dK += dS^T Q over the BQ queries, this wave's output tiles
+    // dV += P^T dO and dK += dS^T Q over the step's 64 queries, channel tiles c
 #pragma unroll
-    for (int a = 0; a < C::TPW; ++a) {
-      const int ot = wave * C::TPW + a;
-      const int ktile = ot & 1, ctile = ot >> 1;  // keys 32 ktile .., channels 32 ctile ..
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int s = 0; s < BQ / 16; ++s) {
-        const bf16x8 ap = tr_operand<C::PROWB, BK>(pt, 16 * s, 32 * ktile, lane);
-        const bf16x8 as = tr_operand<C::PROWB, BK>(st, 16 * s, 32 * ktile, lane);
-        const bf16x8 bg = tr_operand<C::ROWB, D>(gt, 16 * s, 32 * ctile, lane);
-        const bf16x8 bq = tr_operand<C::ROWB, D>(qt, 16 * s, 32 * ctile, lane);
-        acc_v[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bg, acc_v[a], 0, 0, 0);
-        acc_k[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, bq, acc_k[a], 0, 0, 0);
-      }
-    }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          const bf16x8 bg = tr_operand<C::ROWB, D>(gt, 32 * h + 16 * u, 32 * c, lane);
+          const bf16x8 bq = tr_operand<C::ROWB, D>(qt, 32 * h + 16 * u, 32 * c, lane);
+          acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][u], bg, acc_v[c], 0, 0, 0);
+          acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][u], bq, acc_k[c], 0, 0, 0);
+        }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // with no query block, the K/V copies are still in flight
-  __syncthreads();
+#undef SA_KV_ISSUE
+  __syncthreads();  // every wave is done with the last step's buffer
 
-  // epilogue: dK then dV, each staged through LDS as [key][channel] rows
+  // epilogue: dK then dV, staged through LDS as [key][channel] rows. Element i of tile c: channel
+  // 32 c + ln, key 32 w + 8 (i / 4) + 4 hf + i % 4
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
-    for (int a = 0; a < C::TPW; ++a) {
-      const int ot = wave * C::TPW + a;
-      const int ktile = ot & 1, ctile = ot >> 1;
-      const f32x16& acc = which == 0 ? acc_k[a] : acc_v[a];
+    for (int c = 0; c < D / 32; ++c) {
+      const f32x16& acc = which == 0 ? acc_k[c] : acc_v[c];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        // element i: channel 32 ctile + ln, key 32 ktile + 8 (i / 4) + 4 hf + i % 4
-        const int key = 32 * ktile + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const int ch = 32 * ctile + ln;
-        *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base + key * C::OROW + ch * 2) = (__bf16)acc[i];
-        *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base + (key + 1) * C::OROW + ch * 2) =
-            (__bf16)acc[i + 1];
+      for (int i = 0; i < 16; ++i) {
+        const int kr = 32 * wave + 8 * (i >> 2) + 4 * hf + (i & 3);
+        *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base + kr * C::OROW + (32 * c + ln) * 2) =
+            (__bf16)acc[i];
       }
     }
     __syncthreads();
@@ -419,9 +445,9 @@ __global__ __launch_bounds__(BQ * 2, 1) void attn_bwd_dkdv_kernel(
     constexpr int CH16 = D * 2 / 16;
     for (int e = threadIdx.x; e < BK * CH16; e += C::NT) {
       const int r = e / CH16, cc = e % CH16;
-      const int key = kb * BK + r;
-      if (key < N)
-        *reinterpret_cast<u32x4*>(obase + (size_t)key * D * 2 + cc * 16) =
+      const int kr = kb * BK + r;
+      if (kr < N)
+        *reinterpret_cast<u32x4*>(obase + (size_t)kr * D * 2 + cc * 16) =
             *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + r * C::OROW + cc * 16);
     }
     __syncthreads();
@@ -436,7 +462,7 @@ size_t bwd_workspace_bytes(int BH, int N, int Bq) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t nqb = (N + Bq - 1) / Bq, nkb = (N + BK - 1) / BK;
   return al(BH * nqb * nkb * 4) + al(BH * nqb * 4) + al(BH * nkb * nqb * 4) + al(BH * nkb * 4) + al(BH * nkb * nqb) +
-         al((size_t)BH * N * 4);
+         2 * al((size_t)BH * nqb * Bq * 4);
 }
 
 template <int D, int BQ>
@@ -456,7 +482,10 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   p += al((size_t)BH * nkb * 4);
   uint8_t* mask_t = reinterpret_cast<uint8_t*>(p);
   p += al((size_t)BH * nkb * nqb);
-  float* delta = reinterpret_cast<float*>(p);
+  const int NP = nqb * BQ;
+  float* deltap = reinterpret_cast<float*>(p);
+  p += al((size_t)BH * NP * 4);
+  float* lse2p = reinterpret_cast<float*>(p);
 
   hipError_t e = launch_compact(mask, BH * nqb, nkb, ridx, rcnt, stream);
   if (e != hipSuccess) return e;
@@ -464,20 +493,20 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      dim3(256), 0, stream, mask, mask_t, nqb, nkb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_compact(mask_t, BH * nkb, nqb, cidx, ccnt, stream)) != hipSuccess) return e;
-  const long long rows = (long long)BH * N;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const char*>(dout), static_cast<const char*>(o), delta, rows);
+  const long long rows_p = (long long)BH * NP;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows_p * (D / 8) + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const char*>(dout), static_cast<const char*>(o), lse, deltap, lse2p, N, NP, rows_p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const float c_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream, q, k, v,
-                     dout, lse, delta, ridx, rcnt, N, nqb, nkb, scale, c_log2, dq);
+                     dout, lse2p, deltap, ridx, rcnt, N, nqb, nkb, scale, c_log2, dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  using C = BCfg<D, BQ>;
+  using C = KVCfg<D>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, BQ>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BQ>), dim3((unsigned)(BH * nkb)), dim3(C::NT), C::LDS, stream, q, k, v,
-                     dout, lse, delta, cidx, ccnt, N, nqb, nkb, scale, c_log2, dk, dv);
+                     dout, lse2p, deltap, cidx, ccnt, N, nqb, nkb, scale, c_log2, dk, dv);
   return hipGetLastError();
 }
 

@@ -135,7 +135,8 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
                           void* o, float* lse, void* stream);
 
 /* Bytes of device workspace sparse_attn_bwd needs (row and column kept lists with counts, the
- * transposed mask, and one float per query; each part 256-byte aligned). 0 for invalid shapes. */
+ * transposed mask, and two floats per query of the nQB * Bq padded rows: D and the LSE in log2
+ * units; each part 256-byte aligned). 0 for invalid shapes. */
 size_t sparse_attn_bwd_workspace_size(int B, int H, int N, int Bq, int Bk);
 
 /*

@@ -188,7 +188,7 @@ def test_bwd_workspace_size():
     nqb, nkb = 8, 16
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     want = al(bh * nqb * nkb * 4) + al(bh * nqb * 4) + al(bh * nkb * nqb * 4) + al(bh * nkb * 4) + \
-        al(bh * nkb * nqb) + al(bh * n * 4)
+        al(bh * nkb * nqb) + 2 * al(bh * nqb * bq * 4)
     assert lib.sparse_attn_bwd_workspace_size(1, 2, n, bq, 64) == want
     assert lib.sparse_attn_bwd_workspace_size(1, 2, n, 96, 64) == 0
 
