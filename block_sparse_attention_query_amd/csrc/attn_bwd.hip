@@ -256,21 +256,46 @@ struct KVCfg {
   static_assert(64 * OROW <= LDS, "output staging must fit");
 };
 
-// Copies of the 64-row tile sb (token rows 64 sb .. + 63, clamped to N - 1) of a [N][D] bf16
-// tensor into a swizzled LDS tile by the two waves: instruction u of wave w fills the 1 KiB
-// stretch m = w PW + u; lane i fills its bytes 16 i .. + 15, i.e. row (1024 m + 16 i) / ROWB and
-// swizzled chunk slot ((1024 m + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
+// Copies of the 64-row tile sb (token rows 64 sb .. + 63) of a [N][D] bf16 tensor into a
+// swizzled LDS tile by the two waves: instruction u of wave w fills the 1 KiB stretch
+// m = w PW + u; lane i fills its bytes 16 i .. + 15, i.e. row (1024 m + 16 i) / ROWB and swizzled
+// chunk slot ((1024 m + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
+// kv_dma_offsets gives each lane's byte offsets inside a tile; rows past N (only in the last
+// tile) are clamped to N - 1.
 template <int D>
-__device__ __forceinline__ void kv_dma(const char* __restrict__ base, int sb, int N, int wave, int lane, lchar* dst) {
-  constexpr int ROWB = 2 * D, PW = 64 * ROWB / 1024 / 2;
+struct KVDma {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int PW = 64 * ROWB / 1024 / 2;
+};
+
+template <int D>
+__device__ __forceinline__ void kv_dma_offsets(int wave, int lane, uint32_t* off) {
+  constexpr int ROWB = KVDma<D>::ROWB;
 #pragma unroll
-  for (int u = 0; u < PW; ++u) {
-    const int m = wave * PW + u;
-    const int byte = m * 1024 + lane * 16;
+  for (int u = 0; u < KVDma<D>::PW; ++u) {
+    const int byte = (wave * KVDma<D>::PW + u) * 1024 + lane * 16;
     const int row = byte / ROWB;
-    const int chunk = ((byte % ROWB) >> 4) ^ kv_swz<D>(row);
-    const int src = min(sb * 64 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(base + (size_t)src * ROWB + chunk * 16, dst + m * 1024, 16, 0, 0);
+    off[u] = (uint32_t)(row * ROWB + ((((byte % ROWB) >> 4) ^ kv_swz<D>(row)) << 4));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kv_dma(const char* __restrict__ base, int sb, int N, int wave, int lane,
+                                       const uint32_t* off, lchar* dst) {
+  constexpr int ROWB = KVDma<D>::ROWB, PW = KVDma<D>::PW;
+  const char* blk = base + (size_t)sb * 64 * ROWB;
+  if (sb * 64 + 64 <= N) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u)
+      __builtin_amdgcn_global_load_lds(blk + off[u], dst + (wave * PW + u) * 1024, 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int row = ((wave * PW + u) * 1024 + lane * 16) / ROWB;
+      const int over = sb * 64 + row - (N - 1);
+      const uint32_t o = over > 0 ? off[u] - (uint32_t)(over * ROWB) : off[u];
+      __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * PW + u) * 1024, 16, 0, 0);
+    }
   }
 }
 
@@ -313,14 +338,16 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
   const char* gbase = static_cast<const char*>(dout) + head_off;
   const float* l2base = lse2p + (size_t)bh * NP;
   const float* dlbase = deltap + (size_t)bh * NP;
+  uint32_t doff[KVDma<D>::PW];
+  kv_dma_offsets<D>(wave, lane, doff);
   // copies of step t into buffer t & 1: both tiles, then wave 0 the LSE and wave 1 the D values
 #define SA_KV_ISSUE(T_)                                                                                  \
   {                                                                                                      \
     const int t_ = (T_);                                                                                 \
     const int sb_ = min(max(list[t_ / SPB], 0), nqb - 1) * SPB + t_ % SPB;                               \
     lchar* b_ = base + (t_ & 1) * C::BUF;                                                                \
-    kv_dma<D>(qbase, sb_, N, wave, lane, b_);                                                            \
-    kv_dma<D>(gbase, sb_, N, wave, lane, b_ + C::OFF_G);                                                 \
+    kv_dma<D>(qbase, sb_, N, wave, lane, doff, b_);                                                      \
+    kv_dma<D>(gbase, sb_, N, wave, lane, doff, b_ + C::OFF_G);                                           \
     __builtin_amdgcn_global_load_lds((wave == 0 ? l2base : dlbase) + sb_ * 64 + lane, b_ + C::OFF_L + wave * 256, \
                                      4, 0, 0);                                                           \
   }
@@ -363,7 +390,8 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     const lchar* gt = qt + C::OFF_G;
 
     // S = Q K^T and dP = dO V^T for queries 32 h .. 32 h + 31 of the step: element i of lane
-    // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4
+    // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4. The A operands of
+    // channel slice s + 1 are read while the products of slice s run.
     f32x16 sc[2], dp[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -372,15 +400,34 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
         sc[h][i] = 0.f;
         dp[h][i] = 0.f;
       }
+    bf16x8 cur[4], nxt[4];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+    for (int h = 0; h < 2; ++h) {
+      cur[2 * h] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[0] + 32 * h * C::ROWB);
+      cur[2 * h + 1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[0] + 32 * h * C::ROWB);
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      if (s + 1 < D / 16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          nxt[2 * h] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s + 1] + 32 * h * C::ROWB);
+          nxt[2 * h + 1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s + 1] + 32 * h * C::ROWB);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 aq = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s] + 32 * h * C::ROWB);
-        const bf16x8 ag = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s] + 32 * h * C::ROWB);
-        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[s], sc[h], 0, 0, 0);
-        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[s], dp[h], 0, 0, 0);
+        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[2 * h], kf[s], sc[h], 0, 0, 0);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[2 * h + 1], vf[s], dp[h], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+    }
+
+    // the first transposed operands of the dV / dK products, read ahead of the softmax work
+    bf16x8 cg = tr_operand<C::ROWB, D>(gt, 0, 0, lane), cq = tr_operand<C::ROWB, D>(qt, 0, 0, lane);
 
     // P = exp(s - LSE) and dS = P (dP - D) scale, packed to bf16 as A operands: run u of half h
     // takes elements 8 u .. 8 u + 7, i.e. queries 32 h + 16 u + 8 (e / 4) + 4 hf + e % 4
@@ -410,19 +457,27 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
         pa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
         sa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
       }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // dV += P^T dO and dK += dS^T Q over the step's 64 queries, channel tiles c
+    // dV += P^T dO and dK += dS^T Q over the step's 64 queries, item j = (h, u, channel tile c);
+    // the operands of item j + 1 are read while the products of item j run
+    constexpr int NC = D / 32;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const bf16x8 bg = tr_operand<C::ROWB, D>(gt, 32 * h + 16 * u, 32 * c, lane);
-          const bf16x8 bq = tr_operand<C::ROWB, D>(qt, 32 * h + 16 * u, 32 * c, lane);
-          acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][u], bg, acc_v[c], 0, 0, 0);
-          acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][u], bq, acc_k[c], 0, 0, 0);
-        }
+    for (int j = 0; j < 4 * NC; ++j) {
+      const int h = j / (2 * NC), u = (j / NC) & 1, c = j % NC;
+      bf16x8 ng, nq;
+      if (j + 1 < 4 * NC) {
+        const int h1 = (j + 1) / (2 * NC), u1 = ((j + 1) / NC) & 1, c1 = (j + 1) % NC;
+        ng = tr_operand<C::ROWB, D>(gt, 32 * h1 + 16 * u1, 32 * c1, lane);
+        nq = tr_operand<C::ROWB, D>(qt, 32 * h1 + 16 * u1, 32 * c1, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][u], cg, acc_v[c], 0, 0, 0);
+      acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][u], cq, acc_k[c], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      cg = ng;
+      cq = nq;
+    }
   }
 #undef SA_KV_ISSUE
   __syncthreads();  // every wave is done with the last step's buffer
