@@ -16,6 +16,8 @@
 // Kernel 2 (select_kernel) takes one row per workgroup: softmax in place, then orders only the
 // entries that can belong to the kept prefix, a chunked prefix sum for m*, then the mask row and
 // optional lists.
+#include <algorithm>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -25,65 +27,96 @@ namespace sa {
 // S = scale * Qbar Kbar^T per head in float64 on the matrix cores (v_mfma_f64_16x16x4f64). For
 // that instruction lane j holds A[j % 16][j / 16] and B[j / 16][j % 16] of a 16x4 / 4x16 step, and
 // element i of the result holds C[4 i + j / 16][j % 16] (lane layout checked with one-hot
-// operands). A workgroup of 4 waves computes a 64 x 64 tile: the 64 key-block rows of Kbar sit in
-// LDS (two doubles of padding per row put the 32 lanes of each half-wave read -- 16 rows x 2
-// consecutive doubles -- on distinct banks), and wave w
-// keeps its 16 query-block rows of Qbar in registers.
+// operands). A workgroup of 4 waves owns 64 query-block rows of Qbar (wave w keeps rows
+// 16 w .. 16 w + 15 in registers) and walks a chunk of 32-row tiles of Kbar. The tiles pass
+// through two LDS buffers: the next tile's loads are in flight while the current one multiplies,
+// and are stored to the other buffer afterwards. Two doubles of padding per row put the 32 lanes
+// of each half-wave read (16 rows x 2 consecutive doubles) on distinct banks.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int ST = 64;  // output tile edge
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+constexpr int SQ = 64;  // query-block rows per workgroup
+constexpr int SK = 32;  // key-block rows per tile
 
 template <int D>
-__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
-                                                     int nqb, int nkb, double scale, double* __restrict__ s_out) {
+__global__ __launch_bounds__(256, 2) void scores_kernel(const double* __restrict__ qp, const double* __restrict__ kp,
+                                                        int nqb, int nkb, int tiles_per_chunk, double scale,
+                                                        double* __restrict__ s_out) {
   constexpr int LROW = D + 2;
-  __shared__ double kl[ST * LROW];
+  constexpr int PER = SK * D / 2 / 256;  // 16-byte pieces of a tile per thread
+  __shared__ __attribute__((aligned(16))) double kl[2][SK * LROW];
   const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * ST;
-  const int j0 = blockIdx.x * ST;
+  const int i0 = blockIdx.y * SQ;
+  const int ntile = (nkb + SK - 1) / SK;
+  const int t0 = blockIdx.x * tiles_per_chunk;
+  const int t1 = min(ntile, t0 + tiles_per_chunk);
+  if (t0 >= t1) return;
   const double* qh = qp + (size_t)bh * nqb * D;
   const double* kh = kp + (size_t)bh * nkb * D;
   const int tid = threadIdx.x;
-  {
-    // all of this thread's loads first, then the LDS stores (no load waits inside a loop)
-    constexpr int PER = ST * D / 256;
-    double v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / D, c = e % D;
-      v[u] = (j0 + r < nkb) ? kh[(size_t)(j0 + r) * D + c] : 0.0;
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = tid + 256 * u;
-      kl[(e / D) * LROW + e % D] = v[u];
-    }
-  }
   const int wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, kq = lane >> 4;
+
+  // piece u of thread tid: tile row r = e / (D / 2), doubles 2 c .. 2 c + 1, e = tid + 256 u
+  f64x2 v[PER];
+  auto load = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 2), c = e % (D / 2);
+      const int j = t * SK + r;
+      v[u] = j < nkb ? *reinterpret_cast<const f64x2*>(kh + (size_t)j * D + 2 * c) : (f64x2){0.0, 0.0};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 2), c = e % (D / 2);
+      *reinterpret_cast<f64x2*>(&kl[buf][r * LROW + 2 * c]) = v[u];
+    }
+  };
+
+  load(t0);
   const int qrow = i0 + 16 * wave + m;
   double a[D / 4];
 #pragma unroll
   for (int s = 0; s < D / 4; ++s) a[s] = qrow < nqb ? qh[(size_t)qrow * D + 4 * s + kq] : 0.0;
+  store(0);
   __syncthreads();
-  f64x4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = (f64x4){0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-  for (int s = 0; s < D / 4; ++s)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], kl[(16 * t + m) * LROW + 4 * s + kq], acc[t], 0, 0, 0);
+
   double* so = s_out + (size_t)bh * nqb * nkb;
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) load(t + 1);  // in flight during the products
+    f64x4 acc[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int col = j0 + 16 * t + m;
+    for (int h = 0; h < 2; ++h) acc[h] = (f64x4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = i0 + 16 * wave + 4 * i + kq;
-      if (row < nqb && col < nkb) so[(size_t)row * nkb + col] = scale * acc[t][i];
+    for (int s = 0; s < D / 4; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], kl[buf][(16 * h + m) * LROW + 4 * s + kq], acc[h], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = t * SK + 16 * h + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i0 + 16 * wave + 4 * i + kq;
+        if (row < nqb && col < nkb) so[(size_t)row * nkb + col] = scale * acc[h][i];
+      }
     }
+    // the other buffer was last read in step t - 1, which every wave finished before the barrier
+    if (t + 1 < t1) store(buf ^ 1);
+    __syncthreads();
   }
+}
+
+// Key tiles per workgroup: enough workgroups for about four rounds of two per CU.
+inline int scores_tiles_per_chunk(int BH, int nqb, int nkb) {
+  const int ntile = (nkb + SK - 1) / SK;
+  const long long pairs = (long long)BH * ((nqb + SQ - 1) / SQ);
+  const int chunks = (int)std::max(1LL, std::min<long long>(ntile, (2048 + pairs - 1) / pairs));
+  return (ntile + chunks - 1) / chunks;
 }
 
 // ---------------------------------------------------------------- kernel 2: row selection
@@ -587,11 +620,13 @@ size_t select_lds_bytes(int np2) {
 hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, int nkb, int d, double scale,
                          int k, double p, double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt,
                          hipStream_t stream) {
-  const dim3 g1((unsigned)((nkb + ST - 1) / ST), (unsigned)((nqb + ST - 1) / ST), (unsigned)BH);
+  const int tpc = scores_tiles_per_chunk(BH, nqb, nkb);
+  const int ntile = (nkb + SK - 1) / SK;
+  const dim3 g1((unsigned)((ntile + tpc - 1) / tpc), (unsigned)((nqb + SQ - 1) / SQ), (unsigned)BH);
   if (d == 128)
-    hipLaunchKernelGGL((scores_kernel<128>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, scale, probs);
+    hipLaunchKernelGGL((scores_kernel<128>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, tpc, scale, probs);
   else
-    hipLaunchKernelGGL((scores_kernel<64>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, scale, probs);
+    hipLaunchKernelGGL((scores_kernel<64>), g1, dim3(256), 0, stream, qp, kp, nqb, nkb, tpc, scale, probs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nkb <= WAVE_NKB) {
