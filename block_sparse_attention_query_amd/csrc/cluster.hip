@@ -466,7 +466,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
                                                              const int32_t* __restrict__ ntiles, int max_tiles,
                                                              const int32_t* __restrict__ koff, int Cq, int Ck,
                                                              const int32_t* __restrict__ kidx,
-                                                             const int32_t* __restrict__ kcnt, float c_log2,
+                                                             const int32_t* __restrict__ kcnt,
+                                                             const int32_t* __restrict__ qperm, float c_log2,
                                                              void* __restrict__ o, float* __restrict__ lse) {
   using C = DCfg<D, BQ>;
   constexpr int NT = C::NT;
@@ -535,12 +536,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
   lint* rst_l = (lint*)rstart;
   if (ntk > 0) var_gather<D, BQ>(kbase, vbase, 0, L, cum_l, rst_l, trow, choff, cur, wave, buf0);
 
+  // query rows: permuted position qrow; with qperm, Q, O and LSE live in the original token order
+  // and row qrow is token qperm[qrow]
+  const int32_t* qp_h = qperm != nullptr ? qperm + (size_t)bh * N : nullptr;
   const int qrow = qs + wave * 32 + ln;
   const bool qvalid = wave * 32 + ln < qc;
+  const int qtok = qvalid && qp_h != nullptr ? min(max(qp_h[qrow], 0), N - 1) : qrow;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j)
-    qf[j] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * j + 8 * hf) * 2)
+    qf[j] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qtok * D + 16 * j + 8 * hf) * 2)
                                               : make_uint4(0, 0, 0, 0));
   int koffs[D / 16];
   {
@@ -662,12 +667,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
 #pragma unroll
   for (int e = lane; e < 32 * CH16; e += 64) {
     const int r = e / CH16, cc = e % CH16;
-    if (wave * 32 + r < qc)
-      *reinterpret_cast<u32x4*>(obase + (size_t)(qs + wave * 32 + r) * D * 2 + cc * 16) =
+    if (wave * 32 + r < qc) {
+      const int pos = qs + wave * 32 + r;
+      const int tok = qp_h != nullptr ? min(max(qp_h[pos], 0), N - 1) : pos;
+      *reinterpret_cast<u32x4*>(obase + (size_t)tok * D * 2 + cc * 16) =
           *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ol + r * C::OROW + cc * 16);
+    }
   }
   if (lse != nullptr && hf == 0 && qvalid)
-    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    lse[(size_t)bh * N + qtok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------- workspaces and launchers
@@ -751,8 +759,8 @@ size_t cluster_fwd_workspace_bytes(int BH, int N, int Cq, int Ck, int Bq) {
 hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
 
 hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int BH, int N, int d, const int32_t* qoff,
-                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, int Bq, double scale, void* o,
-                              float* lse, void* ws, hipStream_t stream) {
+                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, const int32_t* qperm, int Bq,
+                              double scale, void* o, float* lse, void* ws, hipStream_t stream) {
   const int mt = cluster_max_tiles(N, Cq, Bq);
   char* p = static_cast<char*>(ws);
   int4* tiles = reinterpret_cast<int4*>(p);
@@ -771,7 +779,7 @@ hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int B
 #define SA_VAR(D_, BQ_)                                                                                            \
   if (d == D_ && Bq == BQ_) {                                                                                      \
     hipLaunchKernelGGL((attn_var_kernel<D_, BQ_>), grid, dim3(DCfg<D_, BQ_>::NT), 0, stream, q, k, v, N, tiles, nt,  \
-                       mt, koff, Cq, Ck, kidx, kcnt, c_log2, o, lse);                                              \
+                       mt, koff, Cq, Ck, kidx, kcnt, qperm, c_log2, o, lse);                                       \
     return hipGetLastError();                                                                                      \
   }
   SA_VAR(128, 128)
