@@ -353,11 +353,15 @@ def svg2_bench(args, sa, w, q, k, v, gen_s):
         if ev is not None:
             ev[1].record()
         mask = sa.cluster_select(kq["centroids"], kk["centroids"], kk["offsets"], p)
-        kp, vp = sa.permute_rows(k, kk["perm"]), sa.permute_rows(v, kk["perm"])
+        # Q is read and O written in the original token order through the query permutation; K and
+        # V are either permuted into cluster order first or gathered through the key permutation
+        if args.svg2_permute_kv:
+            kp, vp, k_perm = sa.permute_rows(k, kk["perm"]), sa.permute_rows(v, kk["perm"]), None
+        else:
+            kp, vp, k_perm = k, v, kk["perm"]
         if ev is not None:
             ev[2].record()
-        # Q is read and O written in the original token order through the query permutation
-        o = sa.cluster_fwd(q, kp, vp, kq["offsets"], kk["offsets"], mask, w.bq, q_perm=kq["perm"])
+        o = sa.cluster_fwd(q, kp, vp, kq["offsets"], kk["offsets"], mask, w.bq, q_perm=kq["perm"], k_perm=k_perm)
         if ev is not None:
             ev[3].record()
         return o, kq, kk, mask
@@ -403,12 +407,14 @@ def svg2_bench(args, sa, w, q, k, v, gen_s):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic" + (", smooth values" if args.smooth_v else ""),
         "config": {"workload": f"{w.name}: k-means permutation, {Cq} query / {Ck} key clusters, p = {p}, "
-                               f"{'warm start, 1 iteration' if args.svg2_warm else f'{iters} iterations from evenly spaced tokens'}",
+                               f"{'warm start, 1 iteration' if args.svg2_warm else f'{iters} iterations from evenly spaced tokens'}"
+                               f"{', K / V permuted first' if args.svg2_permute_kv else ''}",
                    "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq, "query_clusters": Cq,
                    "key_clusters": Ck, "p": p, "kmeans_iters": iters, "kept_pair_density": round(pairs / (B * H * N * N), 5),
                    "executed_tflop_per_step": round(flops / 1e12, 4), "tile_tflop_per_step": round(tile_flops / 1e12, 4),
                    "parallelism": "none (1 GPU)"},
-        "ms_per_call": {"kmeans_q+k": round(float(per[0]), 4), "cluster_select+permute_kv": round(float(per[1]), 4),
+        "ms_per_call": {"kmeans_q+k": round(float(per[0]), 4),
+                        ("cluster_select+permute_kv" if args.svg2_permute_kv else "cluster_select"): round(float(per[1]), 4),
                         "cluster_fwd": round(float(per[2]), 4)},
         "cluster_fwd_tflops": round(attn_tf, 2),
         "sampled_rel_l2_error_vs_dense": round(float((sp - ex).norm() / ex.norm()), 5),
@@ -447,6 +453,9 @@ def main(argv=None):
     ap.add_argument("--svg2-clusters", type=float, nargs=3, default=(128, 256, 0.9), metavar=("CQ", "CK", "P"),
                     help="query clusters, key clusters and Top-p threshold of --svg2 (default 128 256 0.9)")
     ap.add_argument("--svg2-iters", type=int, default=3, help="k-means iterations of --svg2 (default 3)")
+    ap.add_argument("--svg2-permute-kv", action="store_true",
+                    help="--svg2: permute K and V into cluster order first instead of gathering their rows "
+                         "through the key permutation")
     ap.add_argument("--svg2-warm", action="store_true",
                     help="with --svg2: start every step from the previous step's centroids, one iteration")
     ap.add_argument("--smooth-v", action="store_true",

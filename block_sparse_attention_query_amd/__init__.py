@@ -337,10 +337,10 @@ def permute_rows(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, out
 
 def cluster_fwd(q, k, v, q_offsets, k_offsets, mask, bq: int = 128, scale: float | None = None,
                 return_lse: bool = False, workspace: torch.Tensor | None = None, out=None,
-                q_perm: torch.Tensor | None = None):
-    """Attention over the variable-size blocks of key-permuted K / V. Q and the output are in the
-    query-permuted order, or in the original token order when ``q_perm`` (the query clustering's
-    ``perm``) is given."""
+                q_perm: torch.Tensor | None = None, k_perm: torch.Tensor | None = None):
+    """Attention over variable-size blocks. Q and the output are in the query-permuted order and
+    K / V in the key-permuted order, or each in the original token order when its permutation
+    (``q_perm`` / ``k_perm``: the clusterings' ``perm``) is given."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     Cq, Ck = q_offsets.shape[-1] - 1, k_offsets.shape[-1] - 1
@@ -351,12 +351,14 @@ def cluster_fwd(q, k, v, q_offsets, k_offsets, mask, bq: int = 128, scale: float
                            q.device)
     o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    if q_perm is not None and (q_perm.dtype != torch.int32 or tuple(q_perm.shape) != (B, H, N)
-                               or not q_perm.is_contiguous() or q_perm.device != q.device):
-        raise ValueError(f"q_perm must be a contiguous int32 [{B}, {H}, {N}] tensor on {q.device}")
+    for name, t in (("q_perm", q_perm), ("k_perm", k_perm)):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous int32 [{B}, {H}, {N}] tensor on {q.device}")
     _lib.check(_lib.lib().sparse_attn_cluster_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], B, H, N, d, q_offsets.data_ptr(), Cq,
-        k_offsets.data_ptr(), Ck, mask.data_ptr(), q_perm.data_ptr() if q_perm is not None else None, bq, scale,
+        k_offsets.data_ptr(), Ck, mask.data_ptr(), q_perm.data_ptr() if q_perm is not None else None,
+        k_perm.data_ptr() if k_perm is not None else None, bq, scale,
         o.data_ptr(), lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if return_lse else o
@@ -369,8 +371,7 @@ def svg2_attention(q, k, v, Cq: int, Ck: int, iters: int, p: float, bq: int = 12
     kq = kmeans(q, Cq, iters, init=init_q)
     kk = kmeans(k, Ck, iters, init=init_k)
     mask = cluster_select(kq["centroids"], kk["centroids"], kk["offsets"], p, scale)
-    kp, vp = permute_rows(k, kk["perm"]), permute_rows(v, kk["perm"])
-    o = cluster_fwd(q, kp, vp, kq["offsets"], kk["offsets"], mask, bq, scale, q_perm=kq["perm"])
+    o = cluster_fwd(q, k, v, kq["offsets"], kk["offsets"], mask, bq, scale, q_perm=kq["perm"], k_perm=kk["perm"])
     if return_info:
         return o, {"kmeans_q": kq, "kmeans_k": kk, "mask": mask}
     return o

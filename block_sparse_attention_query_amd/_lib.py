@@ -36,8 +36,8 @@ SIGNATURES = {
     "sparse_attn_cluster_select": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _d, _vp, _vp, _vp]),
     "sparse_attn_permute_rows": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]),
     "sparse_attn_cluster_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "sparse_attn_cluster_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _d, _vp, _vp,
-                                     _vp, _sz, _vp]),
+    "sparse_attn_cluster_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _d, _vp,
+                                     _vp, _vp, _sz, _vp]),
     "sparse_attn_topk_count": (_i, [_d, _i]),
     "sparse_attn_error_string": (ctypes.c_char_p, [_i]),
     "sparse_attn_last_error": (ctypes.c_char_p, []),

@@ -42,8 +42,9 @@ hipError_t launch_permute_rows(const void* x, const int32_t* perm, int BH, int N
 int cluster_max_tiles(int N, int Cq, int Bq);
 size_t cluster_fwd_workspace_bytes(int BH, int N, int Cq, int Ck, int Bq);
 hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int BH, int N, int d, const int32_t* qoff,
-                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, const int32_t* qperm, int Bq,
-                              double scale, void* o, float* lse, void* ws, hipStream_t stream);
+                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, const int32_t* qperm,
+                              const int32_t* kperm, int Bq, double scale, void* o, float* lse, void* ws,
+                              hipStream_t stream);
 }  // namespace sa
 
 namespace {
@@ -331,8 +332,8 @@ size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int C
 
 int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
                             const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck, const uint8_t* mask,
-                            const int32_t* q_perm, int Bq, double scale, void* o, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const int32_t* q_perm, const int32_t* k_perm, int Bq, double scale, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_offsets || !k_offsets || !mask || !workspace) return fail(SA_ERR_INVALID_ARG, "cluster_fwd: null pointer");
   int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
   if (rc) return rc;
@@ -348,8 +349,8 @@ int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dty
                 need);
   if ((long long)B * H * sa::cluster_max_tiles(N, Cq, Bq) > 0x7fffffffLL)
     return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: too many query tiles");
-  return hip_status(sa::launch_cluster_fwd(q, k, v, B * H, N, d, q_offsets, Cq, k_offsets, Ck, mask, q_perm, Bq, scale,
-                                           o, lse, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(sa::launch_cluster_fwd(q, k, v, B * H, N, d, q_offsets, Cq, k_offsets, Ck, mask, q_perm, k_perm,
+                                           Bq, scale, o, lse, workspace, static_cast<hipStream_t>(stream)),
                     "cluster_fwd launch");
 }
 

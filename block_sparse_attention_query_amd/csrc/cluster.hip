@@ -430,22 +430,32 @@ __global__ __launch_bounds__(KM_MAXC) void cluster_tiles_kernel(const int32_t* _
   if (i == 0) ntiles[bh] = total;
 }
 
-// DMA of key tile t of the stream (and the matching value rows) into dst (K) and dst + TILE (V).
-// Stream position pos lies in the range e with cum[e] <= pos < cum[e + 1]; the lane's cursor
-// cur[u] only moves forward because positions grow with t.
+// Key tile t of the stream: var_rows gives the key row behind each of the lane's DMA pieces
+// (stream position pos lies in the range e with cum[e] <= pos < cum[e + 1]; the lane's cursor
+// cur[u] only moves forward because positions grow with t), var_dma copies those K rows into dst
+// and the matching V rows into dst + TILE.
 template <int D, int BQ>
-__device__ __forceinline__ void var_gather(const char* __restrict__ kbase, const char* __restrict__ vbase, int t,
-                                           int L, const __attribute__((address_space(3))) int* cum,
-                                           const __attribute__((address_space(3))) int* rstart,
-                                           const int (&trow)[DCfg<D, BQ>::PER_WAVE],
-                                           const uint32_t (&choff)[DCfg<D, BQ>::PER_WAVE],
-                                           int (&cur)[DCfg<D, BQ>::PER_WAVE], int wave, lchar* dst) {
+__device__ __forceinline__ void var_rows(int t, int L, const __attribute__((address_space(3))) int* cum,
+                                         const __attribute__((address_space(3))) int* rstart,
+                                         const int (&trow)[DCfg<D, BQ>::PER_WAVE], int (&cur)[DCfg<D, BQ>::PER_WAVE],
+                                         int (&row)[DCfg<D, BQ>::PER_WAVE]) {
   using C = DCfg<D, BQ>;
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
     const int pos = min(t * BK + trow[u], L - 1);
     while (cum[cur[u] + 1] <= pos) ++cur[u];
-    const size_t off = (size_t)(rstart[cur[u]] + pos - cum[cur[u]]) * C::ROWB + choff[u];
+    row[u] = rstart[cur[u]] + pos - cum[cur[u]];
+  }
+}
+
+template <int D, int BQ>
+__device__ __forceinline__ void var_dma(const char* __restrict__ kbase, const char* __restrict__ vbase, int N,
+                                        const int (&row)[DCfg<D, BQ>::PER_WAVE],
+                                        const uint32_t (&choff)[DCfg<D, BQ>::PER_WAVE], int wave, lchar* dst) {
+  using C = DCfg<D, BQ>;
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u) {
+    const size_t off = (size_t)min(max(row[u], 0), N - 1) * C::ROWB + choff[u];
     __builtin_amdgcn_global_load_lds(kbase + off, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vbase + off, dst + C::TILE + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
   }
@@ -467,7 +477,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
                                                              const int32_t* __restrict__ koff, int Cq, int Ck,
                                                              const int32_t* __restrict__ kidx,
                                                              const int32_t* __restrict__ kcnt,
-                                                             const int32_t* __restrict__ qperm, float c_log2,
+                                                             const int32_t* __restrict__ qperm,
+                                                             const int32_t* __restrict__ kperm, float c_log2,
                                                              void* __restrict__ o, float* __restrict__ lse) {
   using C = DCfg<D, BQ>;
   constexpr int NT = C::NT;
@@ -534,7 +545,26 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
   typedef __attribute__((address_space(3))) const int lint;
   lint* cum_l = (lint*)cum;
   lint* rst_l = (lint*)rstart;
-  if (ntk > 0) var_gather<D, BQ>(kbase, vbase, 0, L, cum_l, rst_l, trow, choff, cur, wave, buf0);
+  // rows[] holds the key rows of the next tile to copy: stream rows in the key-permuted order, or,
+  // with kperm (K and V in the original order), the tokens kperm maps them to. Their index loads
+  // are issued one tile ahead and land with the previous tile's copies.
+  const int32_t* kp_h = kperm != nullptr ? kperm + (size_t)bh * N : nullptr;
+  int rows[C::PER_WAVE];
+  if (ntk > 0) {
+    var_rows<D, BQ>(0, L, cum_l, rst_l, trow, cur, rows);
+    if (kp_h != nullptr) {
+#pragma unroll
+      for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = min(max(kp_h[rows[u]], 0), N - 1);
+    }
+    var_dma<D, BQ>(kbase, vbase, N, rows, choff, wave, buf0);
+  }
+  if (ntk > 1) {
+    var_rows<D, BQ>(1, L, cum_l, rst_l, trow, cur, rows);
+    if (kp_h != nullptr) {
+#pragma unroll
+      for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = kp_h[rows[u]];  // clamped where the copy uses it
+    }
+  }
 
   // query rows: permuted position qrow; with qperm, Q, O and LSE live in the original token order
   // and row qrow is token qperm[qrow]
@@ -578,7 +608,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
   for (int t = 0; t < ntk; ++t) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t is resident; every wave is done with tile t - 1
-    if (t + 1 < ntk) var_gather<D, BQ>(kbase, vbase, t + 1, L, cum_l, rst_l, trow, choff, cur, wave, (t & 1) ? buf0 : buf1);
+    if (t + 1 < ntk) {
+      var_dma<D, BQ>(kbase, vbase, N, rows, choff, wave, (t & 1) ? buf0 : buf1);
+      if (t + 2 < ntk) {
+        var_rows<D, BQ>(t + 2, L, cum_l, rst_l, trow, cur, rows);
+        if (kp_h != nullptr) {
+#pragma unroll
+          for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = kp_h[rows[u]];  // clamped where the copy uses it
+        }
+      }
+    }
     const lchar* kt = (t & 1) ? buf1 : buf0;
     lchar* vt = ((t & 1) ? buf1 : buf0) + C::TILE;
     f32x16 s0, s1;
@@ -759,8 +798,9 @@ size_t cluster_fwd_workspace_bytes(int BH, int N, int Cq, int Ck, int Bq) {
 hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
 
 hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int BH, int N, int d, const int32_t* qoff,
-                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, const int32_t* qperm, int Bq,
-                              double scale, void* o, float* lse, void* ws, hipStream_t stream) {
+                              int Cq, const int32_t* koff, int Ck, const uint8_t* mask, const int32_t* qperm,
+                              const int32_t* kperm, int Bq, double scale, void* o, float* lse, void* ws,
+                              hipStream_t stream) {
   const int mt = cluster_max_tiles(N, Cq, Bq);
   char* p = static_cast<char*>(ws);
   int4* tiles = reinterpret_cast<int4*>(p);
@@ -779,7 +819,7 @@ hipError_t launch_cluster_fwd(const void* q, const void* k, const void* v, int B
 #define SA_VAR(D_, BQ_)                                                                                            \
   if (d == D_ && Bq == BQ_) {                                                                                      \
     hipLaunchKernelGGL((attn_var_kernel<D_, BQ_>), grid, dim3(DCfg<D_, BQ_>::NT), 0, stream, q, k, v, N, tiles, nt,  \
-                       mt, koff, Cq, Ck, kidx, kcnt, qperm, c_log2, o, lse);                                       \
+                       mt, koff, Cq, Ck, kidx, kcnt, qperm, kperm, c_log2, o, lse);                                \
     return hipGetLastError();                                                                                      \
   }
   SA_VAR(128, 128)

@@ -306,9 +306,9 @@ size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int C
  * sparse_attn_fwd; a query cluster with no kept key gets O = 0 and LSE = -inf. Queries run in
  * tiles of Bq rows inside each cluster; the kept keys are gathered into 64-row tiles across
  * cluster boundaries, so only the last key tile of a query cluster is partial.
- *   q, k, v     device, [B, H, N, d] SA_BF16: k and v in the key-permuted order (keys by the key
- *               clusters); q in the query-permuted order, or in the original order when q_perm
- *               is given.
+ *   q, k, v     device, [B, H, N, d] SA_BF16: q in the query-permuted order (queries by the query
+ *               clusters) and k, v in the key-permuted order (keys by the key clusters), or each
+ *               in the original token order when its permutation is given.
  *   q_offsets   device, [B, H, Cq + 1] int32; k_offsets device, [B, H, Ck + 1] int32 (ascending,
  *               from 0 to N; not checked).
  *   mask        device, [B, H, Cq, Ck] uint8.
@@ -317,6 +317,9 @@ size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int C
  *               given, q is read and o / lse are written in the original token order through it,
  *               which replaces permuting Q before the call and O after it. Entries are clamped
  *               to [0, N); a q_perm that is not a permutation leaves rows of o unwritten.
+ *   k_perm      device or NULL, [B, H, N] int32: the key permutation. When given, k and v are
+ *               in the original token order and each key row of the stream is fetched through it
+ *               (replacing permuting K and V before the call). Entries are clamped to [0, N).
  *   o           device out, [B, H, N, d] bf16 in the permuted query order (original order with
  *               q_perm); lse device out or NULL, [B, H, N] float32, same order.
  *   workspace   device scratch of at least sparse_attn_cluster_fwd_workspace_size() bytes,
@@ -325,8 +328,8 @@ size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int C
  */
 int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
                             const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck, const uint8_t* mask,
-                            const int32_t* q_perm, int Bq, double scale, void* o, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            const int32_t* q_perm, const int32_t* k_perm, int Bq, double scale, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host helper: the Top-k size for a fraction, as select_mask computes it (-1 if invalid). */
 int sparse_attn_topk_count(double k_frac, int nkb);

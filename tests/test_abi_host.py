@@ -284,8 +284,8 @@ def test_permute_rows_rejects(kw, code):
 
 def _cfwd(**kw):
     ws = _lib.lib().sparse_attn_cluster_fwd_workspace_size(1, 2, 1000, 8, 40, 128)
-    a = dict(q=P, k=P, v=P, dtype=0, B=1, H=2, N=1000, d=64, qo=P, Cq=8, ko=P, Ck=40, mask=P, q_perm=None, Bq=128,
-             scale=0.125, o=P, lse=None, ws=P, ws_bytes=ws, stream=None)
+    a = dict(q=P, k=P, v=P, dtype=0, B=1, H=2, N=1000, d=64, qo=P, Cq=8, ko=P, Ck=40, mask=P, q_perm=None, k_perm=None,
+             Bq=128, scale=0.125, o=P, lse=None, ws=P, ws_bytes=ws, stream=None)
     a.update(kw)
     return _lib.lib().sparse_attn_cluster_fwd(*a.values())
 

@@ -156,10 +156,15 @@ def check_cluster_attention(q, k, v, Cq, Ck, p, bq, label, mask_fn=None, sample=
     o = sa.permute_rows(op, kq["perm"], inverse=True)
     lse = torch.empty_like(lsep)
     lse.scatter_(2, kq["perm"].long(), lsep)
-    # reading Q and writing O / LSE through the query permutation changes addressing only
+    # reading Q / K / V and writing O / LSE through the permutations changes addressing only
     o2, lse2 = sa.cluster_fwd(qd, kp, vp, kq["offsets"], kk["offsets"], mask, bq, return_lse=True, q_perm=kq["perm"])
+    o3, lse3 = sa.cluster_fwd(qd, kd, vd, kq["offsets"], kk["offsets"], mask, bq, return_lse=True, q_perm=kq["perm"],
+                              k_perm=kk["perm"])
+    o4 = sa.cluster_fwd(qp, kd, vd, kq["offsets"], kk["offsets"], mask, bq, k_perm=kk["perm"])
     torch.cuda.synchronize()
     assert torch.equal(o2, o) and torch.equal(lse2, lse), "q_perm path differs from the permuted path"
+    assert torch.equal(o3, o) and torch.equal(lse3, lse), "q_perm + k_perm path differs from the permuted path"
+    assert torch.equal(o4, op), "k_perm path differs from the permuted path"
     lq, lk = kq["labels"].cpu().numpy(), kk["labels"].cpu().numpy()
     m = mask.cpu().numpy()
     want, wlse = svg2.cluster_attention(f64(q), f64(k), f64(v), lq, lk, m, clusters=sample)
