@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const uint16_t* __restri
 }
 
 // Counting sort, pass 1. Grid (BH, ceil(N / 256)): for every token, the number of earlier tokens
-// of its chunk with the same label; per chunk, the count of every label (all C of them).
+// of its chunk with the same label; per chunk, the count of every label (all C of them), stored
+// label-major (hist[bh][label][chunk]) so that each label's counts are contiguous for pass 2.
 __global__ __launch_bounds__(KM_CH) void km_rank_kernel(const int32_t* __restrict__ labels, int N, int C, int nch,
                                                        int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
   __shared__ int lab[KM_CH];
@@ -201,29 +202,49 @@ __global__ __launch_bounds__(KM_CH) void km_rank_kernel(const int32_t* __restric
     atomicAdd(&cnt[my], 1);  // counts only: the order of the additions does not matter
   }
   __syncthreads();
-  int32_t* hrow = hist + ((size_t)bh * nch + ch) * C;
-  for (int c = tid; c < C; c += KM_CH) hrow[c] = cnt[c];
+  int32_t* hh = hist + (size_t)bh * C * nch + ch;
+  for (int c = tid; c < C; c += KM_CH) hh[(size_t)c * nch] = cnt[c];
 }
 
-// Pass 2. Grid BH, 1024 threads (thread = label): exclusive prefix of every label's chunk counts
-// over the chunks (in place), then offsets[c] = the exclusive prefix of the label totals.
-__global__ __launch_bounds__(KM_MAXC) void km_scan_kernel(int32_t* __restrict__ hist, int C, int nch,
-                                                         int32_t* __restrict__ offsets) {
+// Pass 2a. Grid (BH, ceil(C / 16)), 16 waves, one label per wave: exclusive prefix of the label's
+// chunk counts over the chunks, in place (lane l owns a contiguous run of chunks: its run sum, a
+// wave scan of the sums, then the run rewritten), and the label total into offsets[label].
+__global__ __launch_bounds__(1024) void km_scan_kernel(int32_t* __restrict__ hist, int C, int nch,
+                                                      int32_t* __restrict__ offsets) {
+  const int bh = blockIdx.x, lane = threadIdx.x & 63;
+  const int c = blockIdx.y * 16 + (threadIdx.x >> 6);
+  if (c >= C) return;  // whole waves
+  int32_t* h = hist + ((size_t)bh * C + c) * nch;
+  const int per = (nch + 63) / 64;
+  const int k0 = min(nch, lane * per), k1 = min(nch, k0 + per);
+  int sum = 0;
+  for (int k = k0; k < k1; ++k) sum += h[k];
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  int run = inc - sum;
+  for (int k = k0; k < k1; ++k) {
+    const int v = h[k];
+    h[k] = run;
+    run += v;
+  }
+  if (lane == 63) offsets[(size_t)bh * (C + 1) + c] = inc;
+}
+
+// Pass 2b. Grid BH, 1024 threads (thread = label): offsets[c] = the exclusive prefix of the label
+// totals, offsets[C] = N.
+__global__ __launch_bounds__(KM_MAXC) void km_offsets_kernel(int C, int32_t* __restrict__ offsets) {
   __shared__ int scratch[KM_MAXC / 64];
   const int bh = blockIdx.x, c = threadIdx.x;
-  int run = 0;
-  if (c < C) {
-    int32_t* h = hist + (size_t)bh * nch * C + c;
-    for (int k = 0; k < nch; ++k) {
-      const int v = h[(size_t)k * C];
-      h[(size_t)k * C] = run;
-      run += v;
-    }
-  }
+  int32_t* off = offsets + (size_t)bh * (C + 1);
+  const int v = c < C ? off[c] : 0;
   int total;
-  const int ex = block_exclusive_scan<KM_MAXC>(c < C ? run : 0, scratch, &total);
-  if (c < C) offsets[(size_t)bh * (C + 1) + c] = ex;
-  if (c == 0) offsets[(size_t)bh * (C + 1) + C] = total;
+  const int ex = block_exclusive_scan<KM_MAXC>(v, scratch, &total);
+  if (c < C) off[c] = ex;
+  if (c == 0) off[C] = total;
 }
 
 // Pass 3. Grid (BH, ceil(N / 256)): perm[offsets[l] + chunk base[l] + rank] = token.
@@ -236,7 +257,7 @@ __global__ __launch_bounds__(KM_CH) void km_scatter_kernel(const int32_t* __rest
   const int t = ch * KM_CH + threadIdx.x;
   if (t >= N) return;
   const int l = labels[(size_t)bh * N + t];
-  const int pos = offsets[(size_t)bh * (C + 1) + l] + hist[((size_t)bh * nch + ch) * C + l] + rank[(size_t)bh * N + t];
+  const int pos = offsets[(size_t)bh * (C + 1) + l] + hist[((size_t)bh * C + l) * nch + ch] + rank[(size_t)bh * N + t];
   perm[(size_t)bh * N + pos] = t;
 }
 
@@ -754,7 +775,9 @@ hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, 
                        xs, chi, clo, cn, N, CP, labels);                                                           \
     hipLaunchKernelGGL(km_rank_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, N, C, nch, \
                        rank, hist);                                                                                \
-    hipLaunchKernelGGL(km_scan_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, hist, C, nch, offsets);       \
+    hipLaunchKernelGGL(km_scan_kernel, dim3((unsigned)BH, (unsigned)((C + 15) / 16)), dim3(1024), 0, stream, hist, C, \
+                       nch, offsets);                                                                              \
+    hipLaunchKernelGGL(km_offsets_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, C, offsets);              \
     hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, rank,  \
                        hist, offsets, N, C, nch, perm);                                                            \
     hipLaunchKernelGGL((km_update_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(256), 0, stream, xs, perm,     \
