@@ -262,46 +262,60 @@ __global__ __launch_bounds__(KM_CH) void km_scatter_kernel(const int32_t* __rest
 }
 
 // Grid (BH, CP), 256 threads: centroid c = the float64 mean of its tokens (an empty cluster keeps
-// its centroid), then its MFMA operands. Thread (g, ch), g < 256 / D, sums channel ch over the
-// members o0 + g, o0 + g + 256 / D, ... of the cluster's run of the permuted order, eight loads in
-// flight; the partial sums are added in the order of g, so the result is deterministic.
+// its centroid), then its MFMA operands. Thread (r, cs) sums channels 8 cs .. 8 cs + 7 (one
+// 16-byte load per row) over the members o0 + r, o0 + r + RS, ... of the cluster's run of the
+// permuted order, eight rows in flight; the RS partial sums of a channel are added in the order
+// of r, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void km_update_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets, int N, int C, int CP,
                                                         float* __restrict__ cen, __bf16* __restrict__ chi,
                                                         __bf16* __restrict__ clo, float* __restrict__ cn) {
-  constexpr int G = 256 / D;
-  __shared__ double part[G][D];
+  constexpr int LPR = D / 8;    // lanes per row: 16 bytes (8 channels) each
+  constexpr int RS = 256 / LPR;  // row slots: members o0 + r, o0 + r + RS, ... go to slot r
+  __shared__ double part[RS][D];
   __shared__ float red[4];
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int g = tid / D, ch = tid % D;
+  const int r = tid / LPR, cs = tid % LPR;
   int o0 = 0, o1 = 0;
   if (c < C) {
     o0 = offsets[(size_t)bh * (C + 1) + c];
     o1 = offsets[(size_t)bh * (C + 1) + c + 1];
   }
-  const uint16_t* xh = x + (size_t)bh * N * D + ch;
+  const char* xh = reinterpret_cast<const char*>(x) + (size_t)bh * N * D * 2 + cs * 16;
   const int32_t* pp = perm + (size_t)bh * N;
-  double acc = 0.0;
-  int m = o0 + g;
-  for (; m + 7 * G < o1; m += 8 * G) {
-    uint32_t b[8];
+  double acc[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) b[u] = xh[(size_t)pp[m + u * G] * D];
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  auto add = [&](const uint4 w) {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += (double)__uint_as_float(b[u] << 16);
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)__uint_as_float(q[e] << 16);
+      acc[2 * e + 1] += (double)__uint_as_float(q[e] & 0xffff0000u);
+    }
+  };
+  int m = o0 + r;
+  for (; m + 7 * RS < o1; m += 8 * RS) {  // eight gathered rows in flight
+    uint4 b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = *reinterpret_cast<const uint4*>(xh + (size_t)pp[m + u * RS] * D * 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(b[u]);
   }
-  for (; m < o1; m += G) acc += (double)__uint_as_float((uint32_t)xh[(size_t)pp[m] * D] << 16);
-  part[g][ch] = acc;
+  for (; m < o1; m += RS) add(*reinterpret_cast<const uint4*>(xh + (size_t)pp[m] * D * 2));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r][cs * 8 + e] = acc[e];
   __syncthreads();
   float v = 0.f;
+  const int ch = tid;
   if (tid < D && c < C) {
     float* cp = cen + ((size_t)bh * C + c) * D + ch;
     if (o1 > o0) {
-      double s = part[0][ch];
+      double sm = part[0][ch];
 #pragma unroll
-      for (int h = 1; h < G; ++h) s += part[h][ch];
-      v = (float)(s / (double)(o1 - o0));
+      for (int h = 1; h < RS; ++h) sm += part[h][ch];
+      v = (float)(sm / (double)(o1 - o0));
       *cp = v;
     } else {
       v = *cp;
