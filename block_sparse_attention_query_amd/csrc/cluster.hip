@@ -187,23 +187,33 @@ __global__ __launch_bounds__(256) void km_assign_kernel(const uint16_t* __restri
 // label-major (hist[bh][label][chunk]) so that each label's counts are contiguous for pass 2.
 __global__ __launch_bounds__(KM_CH) void km_rank_kernel(const int32_t* __restrict__ labels, int N, int C, int nch,
                                                        int32_t* __restrict__ rank, int32_t* __restrict__ hist) {
+  constexpr int NW = KM_CH / 64;
   __shared__ int lab[KM_CH];
-  __shared__ int cnt[KM_MAXC];
-  const int bh = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x;
+  __shared__ int cnt[NW][KM_MAXC];  // per-wave label counts
+  const int bh = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
   const int t = ch * KM_CH + tid;
-  for (int c = tid; c < C; c += KM_CH) cnt[c] = 0;
+  for (int c = tid; c < C; c += KM_CH)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cnt[w][c] = 0;
   const int my = t < N ? labels[(size_t)bh * N + t] : -1;
   lab[tid] = my;
   __syncthreads();
+  // earlier lanes of this wave with the same label, then the counts of the earlier waves
   int r = 0;
-  for (int u = 0; u < tid; ++u) r += lab[u] == my;
-  if (t < N) {
-    rank[(size_t)bh * N + t] = r;
-    atomicAdd(&cnt[my], 1);  // counts only: the order of the additions does not matter
-  }
+  for (int u = wave * 64; u < tid; ++u) r += lab[u] == my;
+  if (t < N) atomicAdd(&cnt[wave][my], 1);  // counts only: the order of the additions does not matter
   __syncthreads();
+  if (t < N) {
+    for (int w = 0; w < wave; ++w) r += cnt[w][my];
+    rank[(size_t)bh * N + t] = r;
+  }
   int32_t* hh = hist + (size_t)bh * C * nch + ch;
-  for (int c = tid; c < C; c += KM_CH) hh[(size_t)c * nch] = cnt[c];
+  for (int c = tid; c < C; c += KM_CH) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) n += cnt[w][c];
+    hh[(size_t)c * nch] = n;
+  }
 }
 
 // Pass 2a. Grid (BH, ceil(C / 16)), 16 waves, one label per wave: exclusive prefix of the label's
