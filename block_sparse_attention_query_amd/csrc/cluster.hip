@@ -477,32 +477,32 @@ __global__ __launch_bounds__(KM_MAXC) void cluster_tiles_kernel(const int32_t* _
 
 // Key tile t of the stream: var_rows gives the key row behind each of the lane's DMA pieces
 // (stream position pos lies in the range e with cum[e] <= pos < cum[e + 1]; the lane's cursor
-// cur[u] only moves forward because positions grow with t), var_dma copies those K rows into dst
-// and the matching V rows into dst + TILE.
+// cur[u] only moves forward because positions grow with t).
 template <int D, int BQ>
 __device__ __forceinline__ void var_rows(int t, int L, const __attribute__((address_space(3))) int* cum,
-                                         const __attribute__((address_space(3))) int* rstart,
-                                         const int (&trow)[DCfg<D, BQ>::PER_WAVE], int (&cur)[DCfg<D, BQ>::PER_WAVE],
-                                         int (&row)[DCfg<D, BQ>::PER_WAVE]) {
+                                         const __attribute__((address_space(3))) int* rstart, int trow0,
+                                         int (&cur)[DCfg<D, BQ>::PER_WAVE], int (&row)[DCfg<D, BQ>::PER_WAVE]) {
   using C = DCfg<D, BQ>;
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
-    const int pos = min(t * BK + trow[u], L - 1);
+    const int pos = min(t * BK + trow0 + u * (1024 / C::ROWB), L - 1);
     while (cum[cur[u] + 1] <= pos) ++cur[u];
     row[u] = rstart[cur[u]] + pos - cum[cur[u]];
   }
 }
 
+// Copy of one tensor's rows of a key tile (K or V) into dst: var_rows gives the row behind each of
+// the lane's DMA pieces.
 template <int D, int BQ>
-__device__ __forceinline__ void var_dma(const char* __restrict__ kbase, const char* __restrict__ vbase, int N,
-                                        const int (&row)[DCfg<D, BQ>::PER_WAVE],
-                                        const uint32_t (&choff)[DCfg<D, BQ>::PER_WAVE], int wave, lchar* dst) {
+__device__ __forceinline__ void var_dma1(const char* __restrict__ base, int N, const int (&row)[DCfg<D, BQ>::PER_WAVE],
+                                         int trow0, int c0, int wave, lchar* dst) {
   using C = DCfg<D, BQ>;
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
-    const size_t off = (size_t)min(max(row[u], 0), N - 1) * C::ROWB + choff[u];
-    __builtin_amdgcn_global_load_lds(kbase + off, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + off, dst + C::TILE + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
+    // piece u fills tile row trow0 + u (1024 / ROWB), swizzled chunk slot c0
+    const uint32_t choff = (uint32_t)((c0 ^ kv_swz<D>(trow0 + u * (1024 / C::ROWB))) << 4);
+    const size_t off = (size_t)min(max(row[u], 0), N - 1) * C::ROWB + choff;
+    __builtin_amdgcn_global_load_lds(base + off, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
   }
 }
 
@@ -510,10 +510,14 @@ __device__ __forceinline__ void var_dma(const char* __restrict__ kbase, const ch
 // concatenation, in ascending cluster order, of the key ranges [koff[j], koff[j + 1]) of its kept
 // clusters j; cum[] holds the stream position where each range starts. Key tile t covers stream
 // positions 64 t .. 64 t + 63: the DMA lane that fills row r of the tile follows a cursor through
-// the ranges (positions only grow, so it never moves back) and loads key row
-// rstart[e] + pos - cum[e]. Positions past the stream's end are clamped to its last key and get
-// score -inf. The S^T / PV products, the tile layout and the lazy rescale are the forward
-// kernel's.
+// the ranges (positions only grow, so it never moves back) to key row rstart[e] + pos - cum[e] of
+// the key-permuted order, which kperm (when given) maps to the original token. Positions past
+// the stream's end are clamped to its last key and get score -inf.
+// The main loop is the forward kernel's two-stage software pipeline: step t computes the scores
+// of tile t + 1 while the vector units turn the scores of tile t into P and the matrix cores add
+// P V of tile t, so K runs one tile ahead of V. The V rows of tile t + 1 are the rows its K copy
+// used a step earlier, so one cursor set serves both; the row indices of tile t + 2 are loaded
+// one step before their copy is issued.
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                              const void* __restrict__ v, int N,
@@ -527,13 +531,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
                                                              void* __restrict__ o, float* __restrict__ lse) {
   using C = DCfg<D, BQ>;
   constexpr int NT = C::NT;
-  __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];
-  __shared__ __attribute__((aligned(1024))) char buf1_[2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb0_[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1_[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0_[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1_[C::TILE];
   __shared__ int rstart[KM_MAXC];
   __shared__ int cum[KM_MAXC + 1];
   __shared__ int scratch[NT / 64];
-  lchar* const buf0 = (lchar*)buf0_;
-  lchar* const buf1 = (lchar*)buf1_;
+  lchar* const kb0 = (lchar*)kb0_;
+  lchar* const kb1 = (lchar*)kb1_;
+  lchar* const vb0 = (lchar*)vb0_;
+  lchar* const vb1 = (lchar*)vb1_;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = w / max_tiles, tile = w % max_tiles;
@@ -576,38 +584,43 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
   const char* qbase = static_cast<const char*>(q) + head_off;
   const char* kbase = static_cast<const char*>(k) + head_off;
   const char* vbase = static_cast<const char*>(v) + head_off;
-  // this lane's DMA pieces: tile row trow[u], byte offset choff[u] inside the row
-  uint32_t doff[C::PER_WAVE];
-  dma_offsets<D, BQ>(wave, lane, doff);
-  int trow[C::PER_WAVE], cur[C::PER_WAVE];
-  uint32_t choff[C::PER_WAVE];
+  // this lane's DMA pieces: piece u fills 16 bytes of tile row trow0 + u (1024 / ROWB) at chunk
+  // slot c0 (1024-byte stretches hold whole rows, so the slot is the same for every piece)
+  const int trow0 = (wave * C::PER_WAVE * 1024 + lane * 16) / C::ROWB;
+  const int c0 = ((lane * 16) % C::ROWB) >> 4;
+  int cur[C::PER_WAVE];
 #pragma unroll
-  for (int u = 0; u < C::PER_WAVE; ++u) {
-    trow[u] = ((wave * C::PER_WAVE + u) * 1024 + lane * 16) / C::ROWB;
-    choff[u] = doff[u] - (uint32_t)(trow[u] * C::ROWB);
-    cur[u] = 0;
-  }
+  for (int u = 0; u < C::PER_WAVE; ++u) cur[u] = 0;
   typedef __attribute__((address_space(3))) const int lint;
   lint* cum_l = (lint*)cum;
   lint* rst_l = (lint*)rstart;
-  // rows[] holds the key rows of the next tile to copy: stream rows in the key-permuted order, or,
-  // with kperm (K and V in the original order), the tokens kperm maps them to. Their index loads
-  // are issued one tile ahead and land with the previous tile's copies.
   const int32_t* kp_h = kperm != nullptr ? kperm + (size_t)bh * N : nullptr;
-  int rows[C::PER_WAVE];
+  // rk: rows of the next K tile to copy (tile t + 2 inside step t); rv: rows of the next V tile
+  int rk[C::PER_WAVE], rv[C::PER_WAVE];
   if (ntk > 0) {
-    var_rows<D, BQ>(0, L, cum_l, rst_l, trow, cur, rows);
+    var_rows<D, BQ>(0, L, cum_l, rst_l, trow0, cur, rk);
     if (kp_h != nullptr) {
 #pragma unroll
-      for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = min(max(kp_h[rows[u]], 0), N - 1);
+      for (int u = 0; u < C::PER_WAVE; ++u) rk[u] = kp_h[rk[u]];
     }
-    var_dma<D, BQ>(kbase, vbase, N, rows, choff, wave, buf0);
+    var_dma1<D, BQ>(kbase, N, rk, trow0, c0, wave, kb0);
+    var_dma1<D, BQ>(vbase, N, rk, trow0, c0, wave, vb0);
   }
   if (ntk > 1) {
-    var_rows<D, BQ>(1, L, cum_l, rst_l, trow, cur, rows);
+    var_rows<D, BQ>(1, L, cum_l, rst_l, trow0, cur, rk);
     if (kp_h != nullptr) {
 #pragma unroll
-      for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = kp_h[rows[u]];  // clamped where the copy uses it
+      for (int u = 0; u < C::PER_WAVE; ++u) rk[u] = kp_h[rk[u]];
+    }
+    var_dma1<D, BQ>(kbase, N, rk, trow0, c0, wave, kb1);
+#pragma unroll
+    for (int u = 0; u < C::PER_WAVE; ++u) rv[u] = rk[u];
+  }
+  if (ntk > 2) {
+    var_rows<D, BQ>(2, L, cum_l, rst_l, trow0, cur, rk);
+    if (kp_h != nullptr) {
+#pragma unroll
+      for (int u = 0; u < C::PER_WAVE; ++u) rk[u] = kp_h[rk[u]];  // in flight until step 0
     }
   }
 
@@ -650,46 +663,38 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
   float m_run = -INFINITY, l_run = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int t = 0; t < ntk; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t is resident; every wave is done with tile t - 1
-    if (t + 1 < ntk) {
-      var_dma<D, BQ>(kbase, vbase, N, rows, choff, wave, (t & 1) ? buf0 : buf1);
-      if (t + 2 < ntk) {
-        var_rows<D, BQ>(t + 2, L, cum_l, rst_l, trow, cur, rows);
-        if (kp_h != nullptr) {
-#pragma unroll
-          for (int u = 0; u < C::PER_WAVE; ++u) rows[u] = kp_h[rows[u]];  // clamped where the copy uses it
-        }
-      }
-    }
-    const lchar* kt = (t & 1) ? buf1 : buf0;
-    lchar* vt = ((t & 1) ? buf1 : buf0) + C::TILE;
-    f32x16 s0, s1;
+  auto scores = [&](const lchar* kt, f32x16 (&sc)[2]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
+      sc[0][i] = 0.f;
+      sc[1][i] = 0.f;
     }
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
       const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j]);
       const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j] + 32 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], s1, 0, 0, 0);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[j], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[j], sc[1], 0, 0, 0);
     }
-    if (t * BK + BK > L) {  // stream positions past the end
+  };
+  // stream positions past the end (only in the last tile) get score -inf
+  auto mask_tail = [&](f32x16 (&sc)[2], int t) {
+    if (t * BK + BK > L) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int pos = t * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (pos >= L) s0[i] = -INFINITY;
-        if (pos + 32 >= L) s1[i] = -INFINITY;
+        if (pos >= L) sc[0][i] = -INFINITY;
+        if (pos + 32 >= L) sc[1][i] = -INFINITY;
       }
     }
+  };
+  auto block_max = [&](const f32x16 (&sc)[2]) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = partner32_max(mx) * c_log2;
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc[0][i], sc[1][i]));
+    return partner32_max(mx) * c_log2;
+  };
+  auto raise_max = [&](float mx) {
     if (__ballot(mx > m_run + 8.f)) {  // lazy rescale: weights stay below 2^8 between raises
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -700,6 +705,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
         for (int i = 0; i < 16; ++i) oacc[r][i] *= alpha;
       m_run = m_new;
     }
+  };
+  auto accumulate = [&](const f32x16 (&sc)[2], lchar* vt) {
     bf16x8 pb[4];
     float rs = 0.f;
 #pragma unroll
@@ -707,10 +714,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
       uint32_t w0[4], w1[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s0[8 * u + 2 * e + 1], c_log2, -m_run)));
-        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(s1[8 * u + 2 * e + 1], c_log2, -m_run)));
+        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e + 1], c_log2, -m_run)));
+        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e], c_log2, -m_run)),
+                          __builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e + 1], c_log2, -m_run)));
         rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
         rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
       }
@@ -729,13 +736,66 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restr
         const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
       }
+  };
+
+  // Step t: kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1). NEXT: 1 = a full tile
+  // t + 1; 2 = one of the closing steps: tile t + 1 may be the stream's last tile (masked past its
+  // end) or absent.
+  auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
+                  auto next_tag) {
+    constexpr int NEXT = decltype(next_tag)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
+    const bool next = NEXT == 1 || (NEXT == 2 && t + 1 < ntk);
+    if (next) {
+      scores(kn, sn);
+      if constexpr (NEXT == 2) mask_tail(sn, t + 1);
+    }
+    if (t + 2 < ntk) var_dma1<D, BQ>(kbase, N, rk, trow0, c0, wave, kf);
+    if (t + 1 < ntk) var_dma1<D, BQ>(vbase, N, rv, trow0, c0, wave, vf);
+#pragma unroll
+    for (int u = 0; u < C::PER_WAVE; ++u) rv[u] = rk[u];
+    if (t + 3 < ntk) {
+      var_rows<D, BQ>(t + 3, L, cum_l, rst_l, trow0, cur, rk);
+      if (kp_h != nullptr) {
+#pragma unroll
+        for (int u = 0; u < C::PER_WAVE; ++u) rk[u] = kp_h[rk[u]];  // lands with this step's copies
+      }
+    }
+    accumulate(sc, vc);
+    if (next) raise_max(block_max(sn));
+  };
+
+  using full = std::integral_constant<int, 1>;
+  using closing = std::integral_constant<int, 2>;
+  if (ntk > 0) {
+    f32x16 sa[2], sb[2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    scores(kb0, sa);
+    mask_tail(sa, 0);
+    raise_max(block_max(sa));
+    // pairs of steps whose next tiles are both before the last one (S alternates between sa and
+    // sb, the buffers between their even and odd roles); t stays even
+    int t = 0;
+    for (; t + 3 < ntk; t += 2) {
+      step(t, sa, sb, kb1, vb0, kb0, vb1, full{});
+      step(t + 1, sb, sa, kb0, vb1, kb1, vb0, full{});
+    }
+    // one to three closing steps, one code path: buffers chosen by parity, S moved into sa
+    for (; t < ntk; ++t) {
+      const bool odd = (t & 1) != 0;
+      step(t, sa, sb, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1, closing{});
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+    }
   }
   __syncthreads();  // every wave is done with the K / V buffers before they stage the output
 
-  // epilogue: O = O^T / l, staged through LDS (two waves per buffer pair) for row-contiguous stores
+  // epilogue: O = O^T / l, staged through LDS (two waves per buffer) for row-contiguous stores
   const float l_tot = partner32_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  lchar* ol = ((wave & 1) ? buf1 : buf0) + (wave >> 1) * 32 * C::OROW;
+  lchar* ol = ((wave & 1) ? vb0 : kb0) + (wave >> 1) * 32 * C::OROW;
 #pragma unroll
   for (int r = 0; r < D / 32; ++r)
 #pragma unroll
