@@ -713,14 +713,27 @@ __global__ __launch_bounds__(256) void probe_apply_kernel(uint16_t* __restrict__
   for (int e = tid; e < D; e += 256) bias[e] = bias_g[(size_t)bh * D + e];
   char* oh = reinterpret_cast<char*>(o + (size_t)bh * N * D);
   const int t1 = min(N, t0 + rows);
+  // the next 64-row tile of O is loaded into registers while the current one is processed
+  constexpr int PF = 64 * CPR / 256;  // 16-byte pieces per thread
+  static_assert((64 * CPR) % 256 == 0, "whole pieces per thread");
+  uint4 nx[PF];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int e = tid + 256 * u, r = e / CPR, c = e % CPR;
+      nx[u] = r0 + r < t1 ? *reinterpret_cast<const uint4*>(oh + (size_t)(r0 + r) * ROWB + c * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (t0 < t1) load(t0);
   for (int r0 = t0; r0 < t1; r0 += 64) {
     __syncthreads();  // the previous tile's stores have read ot; A^T is resident
-    for (int e = tid; e < 64 * CPR; e += 256) {
-      const int r = e / CPR, c = e % CPR;
-      *reinterpret_cast<uint4*>(ot + r * PADB + c * 16) =
-          r0 + r < N ? *reinterpret_cast<const uint4*>(oh + (size_t)(r0 + r) * ROWB + c * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int e = tid + 256 * u, r = e / CPR, c = e % CPR;
+      *reinterpret_cast<uint4*>(ot + r * PADB + c * 16) = nx[u];
     }
     __syncthreads();
+    if (r0 + 64 < t1) load(r0 + 64);
     f32x16 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
