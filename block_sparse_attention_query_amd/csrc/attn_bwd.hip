@@ -95,7 +95,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const lchar* tile, int row0, int co
 //   dS^T = P^T * (dP^T - D) * scale in registers (the B operand layout of the forward's P^T),
 //   dQ^T += K^T dS^T (K^T by transpose reads of the K tile).
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, const void* __restrict__ dout,
     const float* __restrict__ lse2p, const float* __restrict__ deltap, const int32_t* __restrict__ kidx,
     const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float scale, float c_log2, void* __restrict__ dq) {
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int j = 0; j < 4 * NC; ++j) {
       const int h = j / (2 * NC), u = (j / NC) & 1, c = j % NC;
-      bf16x8 ng, nq;
+      bf16x8 ng = cg, nq = cq;
       if (j + 1 < 4 * NC) {
         const int h1 = (j + 1) / (2 * NC), u1 = ((j + 1) / NC) & 1, c1 = (j + 1) % NC;
         ng = tr_operand<C::ROWB, D>(gt, 32 * h1 + 16 * u1, 32 * c1, lane);

@@ -519,7 +519,7 @@ __device__ __forceinline__ void var_dma1(const char* __restrict__ base, int N, c
 // used a step earlier, so one cursor set serves both; the row indices of tile t + 2 are loaded
 // one step before their copy is issued.
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_var_kernel(const void* __restrict__ q, const void* __restrict__ k,
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_var_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                              const void* __restrict__ v, int N,
                                                              const int4* __restrict__ tiles,
                                                              const int32_t* __restrict__ ntiles, int max_tiles,

@@ -54,7 +54,7 @@ inline int probe_splits(int BH, int P, int nkb) {
 // the range is kept. Writes, per query, the unnormalised output sum_u 2^(c s_u - m) V_u (fp32),
 // its reference m (log2 domain) and the sum l of the same weights. Partial index: (bh S + s) P + p.
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void probe_partial_kernel(const void* __restrict__ q, const void* __restrict__ k,
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void probe_partial_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                                   const void* __restrict__ v, int N, int nqb, int nkb,
                                                                   int P, int S, float c_log2, float* __restrict__ part_o,
                                                                   float* __restrict__ part_ml) {
