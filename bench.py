@@ -124,14 +124,17 @@ def pattern_bench(args, sa, w, q, k, v, gen_s):
     if args.pattern == "squad":
         window = 3 * w.grid[2]  # 3 latent rows: 240 tokens at 720p, about sqrt(N)
         masks = sa.squad_masks(B, H, N, window, w.bq, w.bk, q.device)
-        bufs = [torch.empty_like(q) for _ in range(4)]
-        names = ["window_transpose", "fwd_lists"]
+        bufs = [torch.empty_like(q) for _ in range(4 if args.squad_materialise else 1)]
 
         def step(ev):
             ml, mg = masks
             ev[0].record()
             sa.fwd_lists(q, k, v, ml["kept_idx"], ml["kept_cnt"], w.bq, w.bk, out=bufs[0])   # local pass
             ev[1].record()
+            if not args.squad_materialise:  # global pass reading the window-transposed order in place
+                sa.fwd_lists(q, k, bufs[0], mg["kept_idx"], mg["kept_cnt"], w.bq, w.bk, out=o, window=window)
+                ev[2].record()
+                return
             sa.window_transpose(q, window, out=bufs[1])
             sa.window_transpose(k, window, out=bufs[2])
             sa.window_transpose(bufs[0], window, out=bufs[3])
@@ -142,9 +145,13 @@ def pattern_bench(args, sa, w, q, k, v, gen_s):
             ev[4].record()
 
         mask_list = [m["mask"].cpu().numpy() for m in masks]
-        params = {"window": window, "global_run": N // window}
-        split = lambda e: (e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]),  # noqa: E731
-                           e[1].elapsed_time(e[2]) + e[3].elapsed_time(e[4]))
+        params = {"window": window, "global_run": N // window,
+                  "global_pass": "materialised transposes" if args.squad_materialise else "window-order reads"}
+        if args.squad_materialise:
+            split = lambda e: (e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]),  # noqa: E731
+                               e[1].elapsed_time(e[2]) + e[3].elapsed_time(e[4]))
+        else:
+            split = lambda e: (e[0].elapsed_time(e[2]), 0.0)  # noqa: E731
         metric = "SQuad two-pass (local + global) sparse attention fwd TFLOP/s (executed)"
     else:
         band, period = 3 * w.grid[2], frame
@@ -162,7 +169,7 @@ def pattern_bench(args, sa, w, q, k, v, gen_s):
         metric = "Sparse-vDiT pattern (diagonal + per-frame diagonals + frame-start stripes) sparse attention fwd " \
                  "TFLOP/s (executed)"
     flops = sum(executed_flops(mm, N, w.bq, w.bk, d) for mm in mask_list)
-    nev = 5 if args.pattern == "squad" else 2
+    nev = 5 if args.pattern == "squad" else 2  # the squad step without transposes records 3 of them
     for _ in range(args.warmup):
         step([torch.cuda.Event(enable_timing=True) for _ in range(nev)])
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
@@ -453,6 +460,9 @@ def main(argv=None):
     ap.add_argument("--svg2-clusters", type=float, nargs=3, default=(128, 256, 0.9), metavar=("CQ", "CK", "P"),
                     help="query clusters, key clusters and Top-p threshold of --svg2 (default 128 256 0.9)")
     ap.add_argument("--svg2-iters", type=int, default=3, help="k-means iterations of --svg2 (default 3)")
+    ap.add_argument("--squad-materialise", action="store_true",
+                    help="--pattern squad: write window-transposed copies of Q, K and the local output (and "
+                         "transpose the result back) instead of reading that order in place")
     ap.add_argument("--svg2-permute-kv", action="store_true",
                     help="--svg2: permute K and V into cluster order first instead of gathering their rows "
                          "through the key permutation")

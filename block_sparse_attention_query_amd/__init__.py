@@ -144,8 +144,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, b
 
 def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor, kept_cnt: torch.Tensor,
               bq: int, bk: int = 64, scale: float | None = None, return_lse: bool = False,
-              out: torch.Tensor | None = None):
-    """Block-sparse attention from kept-block lists (as written by ``select_mask(kept_lists=True)``)."""
+              out: torch.Tensor | None = None, window: int | None = None):
+    """Block-sparse attention from kept-block lists (as written by ``select_mask(kept_lists=True)``).
+
+    With ``window``, the attention runs over the window-transposed token order (the lists index
+    its blocks) while q, k, v and the output stay in the original order: the same result as
+    ``window_transpose`` of the inputs, ``fwd_lists`` and the inverse transpose of the output."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
@@ -158,9 +162,14 @@ def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    _lib.check(_lib.lib().sparse_attn_fwd_lists(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype],
-                                                kept_idx.data_ptr(), kept_cnt.data_ptr(), B, H, N, d, bq, bk, scale,
-                                                o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q)))
+    if window is None:
+        _lib.check(_lib.lib().sparse_attn_fwd_lists(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], kept_idx.data_ptr(), kept_cnt.data_ptr(), B,
+            H, N, d, bq, bk, scale, o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q)))
+    else:
+        _lib.check(_lib.lib().sparse_attn_fwd_lists_window(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], kept_idx.data_ptr(), kept_cnt.data_ptr(), B,
+            H, N, d, bq, bk, int(window), scale, o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q)))
     return (o, lse) if return_lse else o
 
 
@@ -217,13 +226,17 @@ def squad_attention(q, k, v, window: int, bq: int, bk: int = 64, scale: float | 
                     return_local: bool = False):
     """Two-pass SQuad attention on the block-sparse kernel: O_local = attention with the local
     mask; then, in the window-transposed token order, attention of (Q, K, O_local) with the global
-    mask, permuted back to raster order."""
+    mask, permuted back to raster order. When the kernel can read that order in place (bf16, Bk 64
+    and at least 64 windows), the global pass does so and no transposed copy is made."""
     B, H, N, d = q.shape
     ml, mg = squad_masks(B, H, N, window, bq, bk, q.device) if masks is None else masks
     o_local = fwd_lists(q, k, v, ml["kept_idx"], ml["kept_cnt"], bq, bk, scale)
-    qt, kt, vt = (window_transpose(t, window) for t in (q, k, o_local))
-    ot = fwd_lists(qt, kt, vt, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale)
-    o = window_transpose(ot, window, inverse=True)
+    if q.dtype == torch.bfloat16 and bk == 64 and N // window >= 64:
+        o = fwd_lists(q, k, o_local, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale, window=window)
+    else:
+        qt, kt, vt = (window_transpose(t, window) for t in (q, k, o_local))
+        ot = fwd_lists(qt, kt, vt, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale)
+        o = window_transpose(ot, window, inverse=True)
     return (o, o_local) if return_local else o
 
 

@@ -23,6 +23,7 @@ SIGNATURES = {
     "sparse_attn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_fwd": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_fwd_lists": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
+    "sparse_attn_fwd_lists_window": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp, _vp, _sz,
                              _vp]),

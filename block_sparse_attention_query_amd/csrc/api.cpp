@@ -20,6 +20,9 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
                        const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
                        hipStream_t stream);
+hipError_t launch_attn_window(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
+                              int BH, int N, int d, int Bq, double scale, int window, void* o, float* lse,
+                              hipStream_t stream);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       const uint8_t* mask, int BH, int N, int d, int Bq, double scale, void* dq, void* dk, void* dv,
                       void* ws, hipStream_t stream);
@@ -184,6 +187,22 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
   return hip_status(sa::launch_attn(q, k, v, dtype, kept_idx, kept_cnt, B * H, N, d, Bq, scale, o, lse,
                                     static_cast<hipStream_t>(stream)),
                     "fwd_lists: attention launch");
+}
+
+int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                                 const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, int window,
+                                 double scale, void* o, float* lse, void* stream) {
+  if (!kept_idx || !kept_cnt) return fail(SA_ERR_INVALID_ARG, "fwd_lists_window: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, o);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: only SA_BF16 tensors are supported");
+  if (Bk != 64) return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: Bk must be 64");
+  if (window <= 0 || N % window != 0) return fail(SA_ERR_INVALID_ARG, "fwd_lists_window: window must divide N");
+  if (N / window < 64)
+    return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: N / window = %d runs; at least 64 are needed", N / window);
+  return hip_status(sa::launch_attn_window(q, k, v, kept_idx, kept_cnt, B * H, N, d, Bq, scale, window, o, lse,
+                                           static_cast<hipStream_t>(stream)),
+                    "fwd_lists_window: attention launch");
 }
 
 int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask, int B, int H, int N,

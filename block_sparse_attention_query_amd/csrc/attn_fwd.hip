@@ -313,6 +313,39 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_staged_kernel(
   }
 }
 
+// ---------------------------------------------------------------- window-transposed rows
+
+// Token of row s of the window-transposed order, whose runs of nw = N / w rows hold the tokens at
+// one position inside their windows of w tokens: (s mod nw) w + s / nw.
+__device__ __forceinline__ int wt_token(int s, int nw, int w) { return (s % nw) * w + s / nw; }
+
+// dma_tile for rows 64 kb .. 64 kb + 63 of the window-transposed order. With nw >= 64 a block
+// spans at most two runs: row i is token ((r0 + i) mod nw) w + p0 (+1 after the wrap), with
+// p0, r0 the run and offset of the block's first row. Rows past N are clamped to row N - 1.
+template <int D, int BQ>
+__device__ __forceinline__ void dma_tile_wt(const char* __restrict__ base, int kb, int N, int nw, int w, int wave,
+                                            const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE], lchar* dst) {
+  using C = DCfg<D, BQ>;
+  const int s0 = kb * BK;
+  const int p0 = s0 / nw, r0 = s0 - p0 * nw;
+  const bool ragged = s0 + BK > N;
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u) {
+    const int i = (int)(off[u] / C::ROWB);
+    const uint32_t choff = off[u] % C::ROWB;
+    int tok;
+    if (!ragged) {
+      const int x = r0 + i;
+      const bool wrap = x >= nw;
+      tok = (wrap ? x - nw : x) * w + p0 + (wrap ? 1 : 0);
+    } else {
+      tok = wt_token(min(s0 + i, N - 1), nw, w);
+    }
+    __builtin_amdgcn_global_load_lds(base + (size_t)tok * C::ROWB + choff, dst + (wave * C::PER_WAVE + u) * 1024, 16,
+                                     0, 0);
+  }
+}
+
 // ---------------------------------------------------------------- bf16 kernel
 
 // Main loop as a two-stage software pipeline over the kept list. Step t computes the scores of
@@ -322,11 +355,15 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_staged_kernel(
 // t, K(t+1) and V(t) are resident and the DMA fills K(t+2) and V(t+1) into the buffers that
 // K(t) and V(t-1) left. The running maximum is raised after P V of block t, from the scores of
 // block t + 1, so the rare rescale branch closes the step instead of splitting it.
-template <int D, int BQ>
+//
+// WT: the rows (queries and keys) are those of the window-transposed order (windows of wt_w
+// tokens, wt_nw = N / wt_w >= 64 of them), read from and written to Q, K, V, O and LSE in the
+// original token order.
+template <int D, int BQ, bool WT = false>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
-    void* __restrict__ o, float* __restrict__ lse) {
+    void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w) {
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
@@ -354,19 +391,25 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
 
   uint32_t doff[C::PER_WAVE];
   dma_offsets<D, BQ>(wave, lane, doff);
+  // K or V block kb into dst: contiguous rows, or rows of the window-transposed order
+  auto copy = [&](const char* base, int kb, lchar* dst) {
+    if constexpr (WT) dma_tile_wt<D, BQ>(base, kb, N, wt_nw, wt_w, wave, doff, dst);
+    else dma_tile<D, BQ>(base, kb, N, wave, lane, doff, dst);
+  };
   if (cnt > 0) {
-    dma_tile<D, BQ>(kbase, blk(0), N, wave, lane, doff, kb0);
-    dma_tile<D, BQ>(vbase, blk(0), N, wave, lane, doff, vb0);
+    copy(kbase, blk(0), kb0);
+    copy(vbase, blk(0), vb0);
   }
-  if (cnt > 1) dma_tile<D, BQ>(kbase, blk(1), N, wave, lane, doff, kb1);
+  if (cnt > 1) copy(kbase, blk(1), kb1);
 
   // Q^T fragments (B operand of S^T): query 32 wave + ln, channels 16 s + 8 hf .. + 7
   const int qrow = qb * BQ + wave * 32 + ln;
   const bool qvalid = qrow < N;
+  const int qtok = WT && qvalid ? wt_token(qrow, wt_nw, wt_w) : qrow;  // the row's token
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    const uint4 x = qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qrow * D + 16 * s + 8 * hf) * 2)
+    const uint4 x = qvalid ? *reinterpret_cast<const uint4*>(qbase + ((size_t)qtok * D + 16 * s + 8 * hf) * 2)
                            : make_uint4(0, 0, 0, 0);
     qf[s] = __builtin_bit_cast(bf16x8, x);
   }
@@ -503,8 +546,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       scores(kn, sn);
       if constexpr (NEXT == 2) mask_tail(sn, blk1);
     }
-    if (blk2 >= 0) dma_tile<D, BQ>(kbase, blk2, N, wave, lane, doff, kf);
-    if (blk1 >= 0) dma_tile<D, BQ>(vbase, blk1, N, wave, lane, doff, vf);
+    if (blk2 >= 0) copy(kbase, blk2, kf);
+    if (blk1 >= 0) copy(vbase, blk1, vf);
     accumulate(sc, vc);
     if constexpr (NEXT != 0) raise_max(block_max(sn));
   };
@@ -566,12 +609,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   for (int e = lane; e < 32 * CH16; e += 64) {
     const int r = e / CH16, cc = e % CH16;
     const int qr = qb * BQ + wave * 32 + r;
-    if (qr < N)
-      *reinterpret_cast<u32x4*>(obase + (size_t)qr * D * 2 + cc * 16) =
+    if (qr < N) {
+      const int tok = WT ? wt_token(qr, wt_nw, wt_w) : qr;
+      *reinterpret_cast<u32x4*>(obase + (size_t)tok * D * 2 + cc * 16) =
           *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(ol + r * C::OROW + cc * 16);
+    }
   }
   if (lse != nullptr && hf == 0 && qvalid) {
-    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    lse[(size_t)bh * N + qtok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -588,7 +633,7 @@ static hipError_t launch_attn_t(const void* q, const void* k, const void* v, con
                                 float* lse, hipStream_t stream) {
   if constexpr (DT == kBF16) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
-                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
+                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0);
   } else {
     hipLaunchKernelGGL((attn_fwd_staged_kernel<DT, D, BQ>), dim3((unsigned)(BH * nqb)), dim3(AttnCfg<DT, D, BQ>::NT),
                        0, stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
@@ -614,6 +659,27 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, c
   SA_ATTN_CASE(kF32, 64, 128)
   SA_ATTN_CASE(kF32, 64, 64)
 #undef SA_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_window(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
+                              int BH, int N, int d, int Bq, double scale, int window, void* o, float* lse,
+                              hipStream_t stream) {
+  const int nqb = (N + Bq - 1) / Bq;
+  const int nkb = (N + BK - 1) / BK;
+  const float c_log2 = (float)(scale * 1.4426950408889634);
+  const int nw = N / window;
+#define SA_WT_CASE(D_, BQ_)                                                                                  \
+  if (d == D_ && Bq == BQ_) {                                                                                \
+    hipLaunchKernelGGL((attn_fwd_kernel<D_, BQ_, true>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D_, BQ_>::NT), 0, \
+                       stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, nw, window);               \
+    return hipGetLastError();                                                                                \
+  }
+  SA_WT_CASE(128, 128)
+  SA_WT_CASE(128, 64)
+  SA_WT_CASE(64, 128)
+  SA_WT_CASE(64, 64)
+#undef SA_WT_CASE
   return hipErrorInvalidValue;
 }
 

@@ -134,6 +134,21 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
                           const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, double scale,
                           void* o, float* lse, void* stream);
 
+/*
+ * sparse_attn_fwd_lists over the window-transposed token order without materialising it: the
+ * attention's rows (queries and keys alike) are those of sparse_attn_window_transpose's forward
+ * order, row s being token (s mod nw) * window + s / nw with nw = N / window, while q, k, v, o
+ * and lse stay in the original token order. kept_idx / kept_cnt index blocks of the transposed
+ * order. This is the SQuad global pass ([SQ] "手法") as a local pass over runs of nw, with the
+ * permutation equivalence of [SVG2] "2. 手法" A; results equal transposing Q, K, V, calling
+ * sparse_attn_fwd_lists and transposing O and LSE back.
+ *   dtype must be SA_BF16 and Bk 64; window must divide N, and N / window must be at least 64
+ *   (a key block then spans at most two runs). Other arguments as sparse_attn_fwd_lists.
+ */
+int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                                 const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, int window,
+                                 double scale, void* o, float* lse, void* stream);
+
 /* Bytes of device workspace sparse_attn_bwd needs (row and column kept lists with counts, the
  * transposed mask, and two floats per query of the nQB * Bq padded rows: D and the LSE in log2
  * units; each part 256-byte aligned). 0 for invalid shapes. */

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -124,6 +124,22 @@ def _fwd_lists(**kw):
 ])
 def test_fwd_lists_rejects(kw, code):
     assert _fwd_lists(**kw) == code
+
+
+def _fwd_lists_window(**kw):
+    a = dict(q=P, k=P, v=P, dtype=0, idx=P, cnt=P, B=1, H=2, N=6400, d=128, Bq=128, Bk=64, window=100, scale=0.125,
+             o=P, lse=None, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_fwd_lists_window(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), -1), (dict(cnt=None), -1), (dict(o=None), -1), (dict(d=48), -2), (dict(Bk=128), -2),
+    (dict(dtype=1), -2), (dict(window=0), -1), (dict(window=-100), -1), (dict(window=99), -1),
+    (dict(window=130), -1), (dict(window=128), -2), (dict(window=200), -2), (dict(H=0), -1),
+])
+def test_fwd_lists_window_rejects(kw, code):
+    assert _fwd_lists_window(**kw) == code
 
 
 def test_last_error_names_the_problem():

@@ -76,7 +76,45 @@ def test_window_transpose_is_the_permutation(dt, n, w):
     assert torch.equal(sa.window_transpose(y, w, inverse=True), x)
 
 
-@pytest.mark.parametrize("n,w,d,bq", [(2048, 64, 64, 128), (2048, 256, 128, 64), (1920, 240, 128, 128)])
+def _random_lists(B, H, nqb, nkb, density, g):
+    """Kept lists (ascending) of a random block mask; query block 0 of head 0 keeps nothing."""
+    m = torch.rand(B, H, nqb, nkb, generator=g) < density
+    m[0, 0, 0] = False
+    idx = torch.zeros(B, H, nqb, nkb, dtype=torch.int32)
+    cnt = m.sum(-1).to(torch.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                kept = torch.nonzero(m[b, h, i]).flatten()
+                idx[b, h, i, :kept.numel()] = kept.to(torch.int32)
+    return idx.to(DEV), cnt.to(DEV)
+
+
+@pytest.mark.parametrize("n,w,d,bq", [(4096, 32, 128, 128), (3000, 40, 128, 64), (4160, 65, 64, 128),
+                                      (6400, 100, 64, 64), (75600, 240, 128, 128)])
+def test_window_order_fwd_is_the_transposed_fwd(n, w, d, bq):
+    """fwd_lists(window=w) reads the window-transposed order in place; it must give, bit for bit,
+    the O and LSE of transposing Q, K, V, running fwd_lists and transposing back."""
+    bk, H = 64, (1 if n > 10000 else 2)
+    g = torch.Generator().manual_seed(n + w)
+    q, k, v = (torch.randn(1, H, n, d, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    if n > 10000:
+        _, mg = sa.squad_masks(1, H, n, w, bq, bk, DEV)
+        idx, cnt = mg["kept_idx"], mg["kept_cnt"]
+    else:
+        idx, cnt = _random_lists(1, H, (n + bq - 1) // bq, (n + bk - 1) // bk, 0.3, g)
+    o, lse = sa.fwd_lists(q, k, v, idx, cnt, bq, bk, return_lse=True, window=w)
+    qt, kt, vt = (sa.window_transpose(t, w) for t in (q, k, v))
+    ot, lt = sa.fwd_lists(qt, kt, vt, idx, cnt, bq, bk, return_lse=True)
+    perm = torch.from_numpy(pt.window_transpose(n, w)).to(DEV)
+    ref_lse = torch.empty_like(lt)
+    ref_lse[:, :, perm] = lt
+    assert torch.equal(o, sa.window_transpose(ot, w, inverse=True))
+    assert torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("n,w,d,bq", [(2048, 64, 64, 128), (2048, 256, 128, 64), (1920, 240, 128, 128),
+                                      (4096, 32, 128, 128), (3000, 40, 64, 64)])
 def test_squad_attention_matches_oracle(n, w, d, bq):
     bk = 64
     g = torch.Generator().manual_seed(w)
