@@ -105,7 +105,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
   lchar* const buf0 = (lchar*)buf0_;
   lchar* const buf1 = (lchar*)buf1_;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
   extern __shared__ __attribute__((aligned(1024))) char lds_[];
   lchar* const base = (lchar*)lds_;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nkb;
   const int kb = tile - bh * nkb;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(BQ * 2) void attn_fwd_staged_kernel(
   using C = AttnCfg<DT, D, BQ>;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
   const int wave = threadIdx.x >> 6;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   lchar* const vb0 = (lchar*)vbuf_;
   lchar* const vb1 = vb0 + C::TILE;
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: SGPR

@@ -45,4 +45,21 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return (w & 7) * per + (w >> 3);
 }
 
+// Row order of the block-sparse attention kernels over their rows (b, h, block). XCD x takes
+// chunks x, x + 8, x + 16, ... of kWorkChunk consecutive rows: each XCD works on neighbouring
+// blocks, which keep mostly the same key (or query) blocks, and on a share of every head, so that
+// heads of very different densities spread evenly over the XCDs (one contiguous range per XCD,
+// as xcd_remap gives, hands whole heads to single XCDs). Rows outside whole chunks are split into
+// one contiguous piece per XCD.
+constexpr int kWorkChunk = 128;
+__device__ __forceinline__ int xcd_chunk_row(int w, int n) {
+  const int per = n >> 3;
+  if (w >= (per << 3)) return w;
+  const int x = w & 7, l = w >> 3;
+  const int full = per / kWorkChunk;
+  const int c = l / kWorkChunk, off = l - c * kWorkChunk;
+  if (c < full) return (c * 8 + x) * kWorkChunk + off;
+  return full * 8 * kWorkChunk + x * (per - full * kWorkChunk) + off;
+}
+
 }  // namespace sa
