@@ -3,8 +3,8 @@
 // Consecutive tokens form a block that is represented by one pooled vector (Sparse VideoGen2
 // page, section "1. 問題定義"); the mean over the block's valid tokens is taken. The kernel is
 // HBM-bound: every Q and K element is read exactly once with 16-byte coalesced loads, summed in
-// float64 (exact for bf16 inputs), reduced across row groups through LDS in a fixed order, and
-// divided once by the valid token count.
+// float64 (exact for bf16 inputs), reduced across row groups by lane shuffles and across the
+// four waves through LDS, and divided once by the valid token count.
 #include "sa_common.h"
 
 namespace sa {
@@ -17,7 +17,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, c
   constexpr int EPV = 16 / ES;             // elements per 16-byte vector
   constexpr int VPR = D / EPV;             // vectors per token row
   constexpr int RG = 256 / VPR;            // token rows covered by one pass of the workgroup
-  __shared__ double red[RG][D + 1];
+  constexpr int MAXR = 128 / RG;           // passes for the largest block (Bq, Bk <= 128)
+  __shared__ double red[4][D];             // one partial sum per wave
 
   int blk = blockIdx.x;
   const char* src;
@@ -43,13 +44,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, c
   const int c = threadIdx.x % VPR;
   const int r0 = threadIdx.x / VPR;
 
+  // every load of the thread is issued before the first sum
+  uint4 v[MAXR];
+#pragma unroll
+  for (int u = 0; u < MAXR; ++u) {
+    const int r = r0 + u * RG;
+    v[u] = r < nvalid ? base[(size_t)r * VPR + c] : make_uint4(0, 0, 0, 0);
+  }
   double acc[EPV];
 #pragma unroll
   for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
-#pragma unroll 8
-  for (int r = r0; r < nvalid; r += RG) {
-    const uint4 v = base[(size_t)r * VPR + c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < MAXR; ++u) {
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     if constexpr (DT == kBF16) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -61,12 +68,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, c
       for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(w[e]);
     }
   }
+  // lanes l, l ^ VPR, l ^ 2 VPR, ... of a wave hold the same channels: sum them by shuffles, then
+  // the four waves through LDS (sums of bf16 values in float64 are exact, so the order is free)
 #pragma unroll
-  for (int e = 0; e < EPV; ++e) red[r0][c * EPV + e] = acc[e];
+  for (int m = VPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane < VPR) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) red[wave][c * EPV + e] = acc[e];
+  }
   __syncthreads();
   if (threadIdx.x < D) {
-    double s = 0.0;
-    for (int g = 0; g < RG; ++g) s += red[g][threadIdx.x];
+    const double s = (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
     dst[threadIdx.x] = s / (double)nvalid;
   }
 }
