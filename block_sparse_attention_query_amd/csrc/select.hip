@@ -27,14 +27,15 @@ namespace sa {
 // S = scale * Qbar Kbar^T per head in float64 on the matrix cores (v_mfma_f64_16x16x4f64). For
 // that instruction lane j holds A[j % 16][j / 16] and B[j / 16][j % 16] of a 16x4 / 4x16 step, and
 // element i of the result holds C[4 i + j / 16][j % 16] (lane layout checked with one-hot
-// operands). A workgroup of 4 waves owns 64 query-block rows of Qbar (wave w keeps rows
-// 16 w .. 16 w + 15 in registers) and walks a chunk of 32-row tiles of Kbar. The tiles pass
+// operands). A workgroup of 4 waves owns 128 query-block rows of Qbar (wave w keeps rows
+// 32 w .. 32 w + 31 in registers, as two sets of 16 that share every Kbar operand read, which
+// gives each wave four independent accumulation chains) and walks a chunk of 32-row tiles of Kbar. The tiles pass
 // through two LDS buffers: the next tile's loads are in flight while the current one multiplies,
 // and are stored to the other buffer afterwards. Two doubles of padding per row put the 32 lanes
 // of each half-wave read (16 rows x 2 consecutive doubles) on distinct banks.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
-constexpr int SQ = 64;  // query-block rows per workgroup
+constexpr int SQ = 128;  // query-block rows per workgroup
 constexpr int SK = 32;  // key-block rows per tile
 
 template <int D>
@@ -77,10 +78,13 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const double* __restrict
   };
 
   load(t0);
-  const int qrow = i0 + 16 * wave + m;
-  double a[D / 4];
+  double a[2][D / 4];
 #pragma unroll
-  for (int s = 0; s < D / 4; ++s) a[s] = qrow < nqb ? qh[(size_t)qrow * D + 4 * s + kq] : 0.0;
+  for (int g = 0; g < 2; ++g) {
+    const int qrow = i0 + 32 * wave + 16 * g + m;
+#pragma unroll
+    for (int s = 0; s < D / 4; ++s) a[g][s] = qrow < nqb ? qh[(size_t)qrow * D + 4 * s + kq] : 0.0;
+  }
   store(0);
   __syncthreads();
 
@@ -88,23 +92,30 @@ __global__ __launch_bounds__(256, 2) void scores_kernel(const double* __restrict
   for (int t = t0; t < t1; ++t) {
     const int buf = (t - t0) & 1;
     if (t + 1 < t1) load(t + 1);  // in flight during the products
-    f64x4 acc[2];
+    f64x4 acc[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) acc[h] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[g][h] = (f64x4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < D / 4; ++s)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[h] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], kl[buf][(16 * h + m) * LROW + 4 * s + kq], acc[h], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const double b = kl[buf][(16 * h + m) * LROW + 4 * s + kq];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int col = t * SK + 16 * h + m;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = i0 + 16 * wave + 4 * i + kq;
-        if (row < nqb && col < nkb) so[(size_t)row * nkb + col] = scale * acc[h][i];
+        for (int g = 0; g < 2; ++g) acc[g][h] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[g][s], b, acc[g][h], 0, 0, 0);
       }
-    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = t * SK + 16 * h + m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = i0 + 32 * wave + 16 * g + 4 * i + kq;
+          if (row < nqb && col < nkb) so[(size_t)row * nkb + col] = scale * acc[g][h][i];
+        }
+      }
     // the other buffer was last read in step t - 1, which every wave finished before the barrier
     if (t + 1 < t1) store(buf ^ 1);
     __syncthreads();
