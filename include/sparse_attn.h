@@ -13,9 +13,13 @@
  *          (ai-papers.net), sections "Top-kとTop-pの限界を解剖する" and
  *          "ハイブリッドマスキングと蒸留微調整".
  *   [SVG2] "Sparse VideoGen2: Accelerate Video Generation with Sparse Attention via
- *          Semantic-Aware Permutation" (gist.science), sections "1. 問題定義" and "2. 手法" B, C.
+ *          Semantic-Aware Permutation" (gist.science), sections "1. 問題定義" and "2. 手法" A, B, C.
  *   [SPR]  "Partition the Support, Reconstruct the Residual: Training-Free Sparse Attention for
  *          Video Generation and World Models" (physicalainews.jp), original abstract.
+ *   [SQ]   "SQuad: Sub-Quadratic Attention Distillation for Efficient Video Generation"
+ *          (gist.science), section "手法".
+ *   [SVD]  "Sparse-vDiT: Unleashing the Power of Sparse Attention to Accelerate Video Diffusion
+ *          Transformers" (aibr.jp), section "3. 中核となる技術的要素".
  *
  * Conventions for every call:
  *   - Pointers marked "device" are device memory on the current HIP device; all tensors are
