@@ -284,16 +284,23 @@ __device__ __forceinline__ void kv_dma(const char* __restrict__ base, int sb, in
                                        const uint32_t* off, lchar* dst) {
   constexpr int ROWB = KVDma<D>::ROWB, PW = KVDma<D>::PW;
   const char* blk = base + (size_t)sb * 64 * ROWB;
+  // The empty asm marks each 32-bit offset as redefined at its use, so that the compiler cannot
+  // hoist 64-bit zero-extended copies of the offsets out of the walk; the copy then takes the
+  // uniform base in SGPRs and the 32-bit offset in one VGPR.
   if (sb * 64 + 64 <= N) {
 #pragma unroll
-    for (int u = 0; u < PW; ++u)
-      __builtin_amdgcn_global_load_lds(blk + off[u], dst + (wave * PW + u) * 1024, 16, 0, 0);
+    for (int u = 0; u < PW; ++u) {
+      uint32_t o = off[u];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * PW + u) * 1024, 16, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int row = ((wave * PW + u) * 1024 + lane * 16) / ROWB;
       const int over = sb * 64 + row - (N - 1);
-      const uint32_t o = over > 0 ? off[u] - (uint32_t)(over * ROWB) : off[u];
+      uint32_t o = over > 0 ? off[u] - (uint32_t)(over * ROWB) : off[u];
+      asm volatile("" : "+v"(o));
       __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * PW + u) * 1024, 16, 0, 0);
     }
   }
