@@ -357,6 +357,8 @@ int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dty
   int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
   if (rc) return rc;
   if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: only SA_BF16 tensors are supported");
+  if ((long long)N * d * 2 > 0xffffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: one head's rows (N * d * 2 bytes) must stay below 4 GiB");
   if (Cq <= 0 || Ck <= 0 || Cq > N || Ck > N) return fail(SA_ERR_INVALID_ARG, "cluster_fwd: cluster counts must lie in [1, N]");
   if (Cq > SA_MAX_CLUSTERS || Ck > SA_MAX_CLUSTERS)
     return fail(SA_ERR_UNSUPPORTED, "cluster_fwd: cluster counts exceed %d", SA_MAX_CLUSTERS);

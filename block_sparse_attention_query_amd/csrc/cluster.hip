@@ -501,7 +501,10 @@ __device__ __forceinline__ void var_dma1(const char* __restrict__ base, int N, c
   for (int u = 0; u < C::PER_WAVE; ++u) {
     // piece u fills tile row trow0 + u (1024 / ROWB), swizzled chunk slot c0
     const uint32_t choff = (uint32_t)((c0 ^ kv_swz<D>(trow0 + u * (1024 / C::ROWB))) << 4);
-    const size_t off = (size_t)min(max(row[u], 0), N - 1) * C::ROWB + choff;
+    // a 32-bit lane offset from the uniform head base (one head's rows stay below 4 GiB); the
+    // empty asm keeps the compiler from widening it to a 64-bit per-lane address
+    uint32_t off = (uint32_t)min(max(row[u], 0), N - 1) * C::ROWB + choff;
+    asm volatile("" : "+v"(off));
     __builtin_amdgcn_global_load_lds(base + off, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
   }
 }

@@ -309,6 +309,7 @@ def _cfwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(qo=None), -1), (dict(mask=None), -1), (dict(ws=None), -1), (dict(ws_bytes=64), -1), (dict(o=None), -1),
     (dict(Cq=0), -1), (dict(Ck=1001), -1), (dict(dtype=1), -2), (dict(Bq=32), -2), (dict(scale=-1.0), -1),
+    (dict(N=20_000_000, d=128), -2),
 ])
 def test_cluster_fwd_rejects(kw, code):
     assert _cfwd(**kw) == code
