@@ -198,6 +198,8 @@ int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, in
   if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: only SA_BF16 tensors are supported");
   if (Bk != 64) return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: Bk must be 64");
   if (window <= 0 || N % window != 0) return fail(SA_ERR_INVALID_ARG, "fwd_lists_window: window must divide N");
+  if ((long long)N * d * 2 > 0xffffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: one head's rows (N * d * 2 bytes) must stay below 4 GiB");
   if (N / window < 64)
     return fail(SA_ERR_UNSUPPORTED, "fwd_lists_window: N / window = %d runs; at least 64 are needed", N / window);
   return hip_status(sa::launch_attn_window(q, k, v, kept_idx, kept_cnt, B * H, N, d, Bq, scale, window, o, lse,

@@ -341,8 +341,11 @@ __device__ __forceinline__ void dma_tile_wt(const char* __restrict__ base, int k
     } else {
       tok = wt_token(min(s0 + i, N - 1), nw, w);
     }
-    __builtin_amdgcn_global_load_lds(base + (size_t)tok * C::ROWB + choff, dst + (wave * C::PER_WAVE + u) * 1024, 16,
-                                     0, 0);
+    // a 32-bit lane offset from the uniform head base (one head's rows stay below 4 GiB), kept
+    // 32-bit by the empty asm so that the copy takes the base from SGPRs
+    uint32_t o = (uint32_t)tok * C::ROWB + choff;
+    asm volatile("" : "+v"(o));
+    __builtin_amdgcn_global_load_lds(base + o, dst + (wave * C::PER_WAVE + u) * 1024, 16, 0, 0);
   }
 }
 

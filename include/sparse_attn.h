@@ -147,7 +147,8 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
  * permutation equivalence of [SVG2] "2. 手法" A; results equal transposing Q, K, V, calling
  * sparse_attn_fwd_lists and transposing O and LSE back.
  *   dtype must be SA_BF16 and Bk 64; window must divide N, and N / window must be at least 64
- *   (a key block then spans at most two runs). Other arguments as sparse_attn_fwd_lists.
+ *   (a key block then spans at most two runs); one head's rows (N * d * 2 bytes) must stay below
+ *   4 GiB. Other arguments as sparse_attn_fwd_lists.
  */
 int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
                                  const int32_t* kept_cnt, int B, int H, int N, int d, int Bq, int Bk, int window,
@@ -343,7 +344,8 @@ size_t sparse_attn_cluster_fwd_workspace_size(int B, int H, int N, int Cq, int C
  *               q_perm); lse device out or NULL, [B, H, N] float32, same order.
  *   workspace   device scratch of at least sparse_attn_cluster_fwd_workspace_size() bytes,
  *               256-byte aligned; overwritten.
- * d in {64, 128}, Bq in {64, 128}, 1 <= Cq, Ck <= min(N, SA_MAX_CLUSTERS).
+ * d in {64, 128}, Bq in {64, 128}, 1 <= Cq, Ck <= min(N, SA_MAX_CLUSTERS); one head's rows
+ * (N * d * 2 bytes) must stay below 4 GiB (SA_ERR_UNSUPPORTED otherwise).
  */
 int sparse_attn_cluster_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d,
                             const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck, const uint8_t* mask,

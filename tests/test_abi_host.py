@@ -137,6 +137,7 @@ def _fwd_lists_window(**kw):
     (dict(idx=None), -1), (dict(cnt=None), -1), (dict(o=None), -1), (dict(d=48), -2), (dict(Bk=128), -2),
     (dict(dtype=1), -2), (dict(window=0), -1), (dict(window=-100), -1), (dict(window=99), -1),
     (dict(window=130), -1), (dict(window=128), -2), (dict(window=200), -2), (dict(H=0), -1),
+    (dict(N=20_000_000, window=200), -2),
 ])
 def test_fwd_lists_window_rejects(kw, code):
     assert _fwd_lists_window(**kw) == code
