@@ -5,44 +5,13 @@
 // of the block-sparse attention for the same mask. With s = scale Q K^T over the kept keys,
 // P = exp(s - LSE) (LSE saved by the forward), D = rowsum(dO * O):
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
-// Three passes: D per query; dQ per query block over its kept key blocks (the forward's walk);
-// dK, dV per key block over the query blocks that keep it (the mask's columns). Every output
+// Two passes: dQ per query block over its kept key blocks (the forward's walk), which also computes
+// D and LSE * log2(e) for its queries and publishes them; then dK, dV per key block over the query
+// blocks that keep it (the mask's columns). Every output
 // element is written by exactly one workgroup, in a fixed order: no atomics, bitwise repeatable.
 #include "attn_tiles.h"
 
 namespace sa {
-
-// ---------------------------------------------------------------- D = rowsum(dO * O)
-
-// D = rowsum(dO * O) and LSE * log2(e) for every query of the padded query blocks (NP per head):
-// rows past N get D = 0 and LSE = +inf, so that their P and dS vanish without a mask.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const char* __restrict__ dout, const char* __restrict__ o,
-                                                        const float* __restrict__ lse, float* __restrict__ deltap,
-                                                        float* __restrict__ lse2p, int N, int NP, long long rows_p) {
-  constexpr int VPR = D / 8;  // 16-byte chunks per bf16 row; VPR lanes reduce one row
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long r = e / VPR;
-  const int c = (int)(e % VPR);
-  const long long bh = r / NP;
-  const int qi = (int)(r - bh * NP);
-  const bool valid = r < rows_p && qi < N;
-  const size_t row = (size_t)bh * N + qi;
-  float acc = 0.f;
-  if (valid) {
-    const uint4 a = *reinterpret_cast<const uint4*>(dout + row * D * 2 + c * 16);
-    const uint4 b = *reinterpret_cast<const uint4*>(o + row * D * 2 + c * 16);
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc += bf16_lo(wa[i]) * bf16_lo(wb[i]) + bf16_hi(wa[i]) * bf16_hi(wb[i]);
-  }
-#pragma unroll
-  for (int off = VPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (r < rows_p && c == 0) {
-    deltap[r] = acc;
-    lse2p[r] = valid ? lse[row] * 1.4426950408889634f : INFINITY;
-  }
-}
 
 // ---------------------------------------------------------------- mask columns
 
@@ -97,7 +66,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const lchar* tile, int row0, int co
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, const void* __restrict__ dout,
-    const float* __restrict__ lse2p, const float* __restrict__ deltap, const int32_t* __restrict__ kidx,
+    const void* __restrict__ o, const float* __restrict__ lse, float* __restrict__ lse2p, float* __restrict__ deltap,
+    const int32_t* __restrict__ kidx,
     const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float scale, float c_log2, void* __restrict__ dq) {
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char buf0_[2 * C::TILE];  // [K | V], even blocks
@@ -138,8 +108,29 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(qbase + off) : make_uint4(0, 0, 0, 0));
     gf[s] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const uint4*>(gbase + off) : make_uint4(0, 0, 0, 0));
   }
-  const float lse2 = lse2p[(size_t)bh * nqb * BQ + qrow];  // +inf past N
-  const float dlt = deltap[(size_t)bh * nqb * BQ + qrow];
+  // D = rowsum(dO * O) of query qrow: this lane holds channels 16 s + 8 hf .. + 7 of dO, the lane
+  // 32 apart the others. Rows past N (padding of the last block) get D = 0 and LSE = +inf, so
+  // that their P and dS vanish without a mask. Both values go to deltap / lse2p (NP = nQB * BQ
+  // per head) for the dK/dV pass; every padded row belongs to exactly one workgroup and lane.
+  float dpart = 0.f;
+  {
+    const char* obase = static_cast<const char*>(o) + head_off;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const size_t off = ((size_t)qrow * D + 16 * s + 8 * hf) * 2;
+      const uint4 ov = qvalid ? *reinterpret_cast<const uint4*>(obase + off) : make_uint4(0, 0, 0, 0);
+      const uint4 gv = __builtin_bit_cast(uint4, gf[s]);
+      const uint32_t wa[4] = {gv.x, gv.y, gv.z, gv.w}, wb[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dpart += bf16_lo(wa[i]) * bf16_lo(wb[i]) + bf16_hi(wa[i]) * bf16_hi(wb[i]);
+    }
+  }
+  const float dlt = partner32_sum(dpart);
+  const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * 1.4426950408889634f : INFINITY;
+  if (hf == 0) {
+    lse2p[(size_t)bh * nqb * BQ + qrow] = lse2;
+    deltap[(size_t)bh * nqb * BQ + qrow] = dlt;
+  }
 
   int koff[D / 16];
   {
@@ -555,13 +546,9 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      dim3(256), 0, stream, mask, mask_t, nqb, nkb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_compact(mask_t, BH * nkb, nqb, cidx, ccnt, stream)) != hipSuccess) return e;
-  const long long rows_p = (long long)BH * NP;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows_p * (D / 8) + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const char*>(dout), static_cast<const char*>(o), lse, deltap, lse2p, N, NP, rows_p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const float c_log2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream, q, k, v,
-                     dout, lse2p, deltap, ridx, rcnt, N, nqb, nkb, scale, c_log2, dq);
+                     dout, o, lse, lse2p, deltap, ridx, rcnt, N, nqb, nkb, scale, c_log2, dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   using C = KVCfg<D>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, BQ>),
