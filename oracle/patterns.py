@@ -27,15 +27,20 @@ Token-level patterns (t a query token, u a key token, all indices 0-based in ras
 * stripe(P):         u mod P == 0 (every query sees the key tokens that start a period)
 
 A block mask keeps block pair (i, j) when at least one (query token of block i, key token of
-block j) pair satisfies the pattern: the block-granular cover of the token pattern, which is what
-a block-sparse kernel can run. Here it is found by brute force over all token pairs.
+block j) pair satisfies the pattern: the block-granular cover of the token pattern, i.e. the
+tiles a block-sparse kernel visits. Here it is found by brute force over all token pairs.
+
+The SQuad operator itself is token-exact: each pass attends over exactly the key tokens its
+token pattern admits (``squad_local``, ``squad_global``), never over a block cover.
 """
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
-from .oracle import block_sizes, masked_attention, num_blocks
+from .oracle import attend_block, block_sizes, num_blocks
 
 LOCAL, GLOBAL, DIAG, MULTIDIAG, STRIPE = 1, 2, 4, 8, 16
 
@@ -86,27 +91,72 @@ def window_transpose(n: int, w: int) -> np.ndarray:
     return (s % nw) * w + s // nw
 
 
-def squad_attention(q, k, v, window: int, bq: int, bk: int, scale: float | None = None):
-    """Two-pass SQuad composition ([SQ] "手法") on block masks:
+def _attend_set(q_rows, k_rows, v_rows, scale: float):
+    """Softmax attention of every query row over exactly the given key rows: the pattern admits
+    those keys and no other, so this is the masked dense row with the other keys at -inf (their
+    exponentials are exactly zero). Returns (O, LSE natural log)."""
+    return attend_block(q_rows, k_rows, v_rows, np.ones(np.shape(k_rows)[0], dtype=bool), scale)
 
-    1. local pass: masked attention of (Q, K, V) with the local(w) block mask;
-    2. global pass: in the window-transposed token order, where the tokens that share a position
-       inside their window form contiguous runs of n / w, masked attention of (Q, K, O_local) with
-       the local(n / w) block mask, i.e. the global(w) pattern, then the output is put back in
-       raster order ([SVG2] "2. 手法" A).
 
-    Returns (O, O_local); arrays are ``[B, H, N, d]`` float64."""
-    n = np.shape(q)[-2]
-    m_local = pattern_block_mask(LOCAL, n, bq, bk, window=window)
-    shp = np.shape(q)[:2] + m_local.shape
-    o_local, _ = masked_attention(q, k, v, np.broadcast_to(m_local, shp), bq, bk, scale)
-    perm = window_transpose(n, window)
-    m_glob = pattern_block_mask(LOCAL, n, bq, bk, window=n // window)
-    qp, kp, vp = (np.asarray(x, dtype=np.float64)[..., perm, :] for x in (q, k, o_local))
-    o_perm, _ = masked_attention(qp, kp, vp, np.broadcast_to(m_glob, shp), bq, bk, scale)
-    o = np.empty_like(o_perm)
-    o[..., perm, :] = o_perm
-    return o, o_local
+def squad_local(q, k, v, window: int, scale: float | None = None, windows=None):
+    """SQuad local pass ([SQ] "手法", "1. SQuad アテンション・オペレーター"): token t attends to
+    the tokens u of its own window of ``window`` consecutive raster tokens, floor(t / w) ==
+    floor(u / w); the last window is partial when w does not divide N.
+
+    ``windows`` optionally restricts the work to some window indices (other rows stay NaN).
+    Returns (O, LSE), ``[B, H, N, d]`` and ``[B, H, N]`` float64."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    b_, h_, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = np.full((b_, h_, n, v.shape[-1]), np.nan)
+    lse = np.full((b_, h_, n), np.nan)
+    nwin = -(-n // window)
+    for b in range(b_):
+        for h in range(h_):
+            for c in (range(nwin) if windows is None else windows):
+                rows = slice(c * window, min(n, (c + 1) * window))
+                o[b, h, rows], lse[b, h, rows] = _attend_set(q[b, h, rows], k[b, h, rows], v[b, h, rows], scale)
+    return o, lse
+
+
+def squad_global(q, k, v, window: int, scale: float | None = None, positions=None):
+    """SQuad global pass ([SQ] "手法"): token t attends to the tokens u at the same relative
+    position inside their windows, t mod w == u mod w, across all windows.
+
+    ``positions`` optionally restricts the work to some positions r in [0, w) (the rows t with
+    t mod w == r; other rows stay NaN). Returns (O, LSE) as ``squad_local``."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    b_, h_, n, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = np.full((b_, h_, n, v.shape[-1]), np.nan)
+    lse = np.full((b_, h_, n), np.nan)
+    for b in range(b_):
+        for h in range(h_):
+            for r in (range(min(window, n)) if positions is None else positions):
+                rows = np.arange(r, n, window)
+                o[b, h, rows], lse[b, h, rows] = _attend_set(q[b, h, rows], k[b, h, rows], v[b, h, rows], scale)
+    return o, lse
+
+
+def squad_attention(q, k, v, window: int, scale: float | None = None, positions=None):
+    """Two-pass SQuad operator ([SQ] "手法"): the local pass of (Q, K, V), then the global pass
+    of (Q, K, O_local): the local output is the global pass's value stream; queries and keys
+    are the same in both passes (the distilled projections are out of scope).
+
+    The local pass is computed for every window, since each position class takes one token from
+    every window. ``positions`` restricts the global pass (a sample). Returns
+    (O, O_local, LSE, LSE_local) in float64."""
+    o_local, lse_local = squad_local(q, k, v, window, scale)
+    o, lse = squad_global(q, k, o_local, window, scale, positions)
+    return o, o_local, lse, lse_local
+
+
+def squad_pairs(n: int, window: int) -> int:
+    """(query, key) token pairs the two SQuad passes attend over: the squared window lengths plus
+    the squared position-class sizes. N w + N^2 / w when w divides N."""
+    wl = np.array([min(window, n - c * window) for c in range(-(-n // window))], dtype=np.int64)
+    pc = np.array([len(range(r, n, window)) for r in range(min(window, n))], dtype=np.int64)
+    return int((wl * wl).sum() + (pc * pc).sum())
 
 
 def block_density(mask: np.ndarray) -> float:
@@ -114,4 +164,5 @@ def block_density(mask: np.ndarray) -> float:
 
 
 __all__ = ["LOCAL", "GLOBAL", "DIAG", "MULTIDIAG", "STRIPE", "token_pattern", "pattern_block_mask",
-           "window_transpose", "squad_attention", "block_density", "block_sizes"]
+           "window_transpose", "squad_local", "squad_global", "squad_attention", "squad_pairs", "block_density",
+           "block_sizes"]

@@ -1,6 +1,6 @@
 """CPU pins of the fixed-pattern oracle (oracle/patterns.py): closed forms of the block covers,
-direct per-window / per-residue attention for the two SQuad passes, and planted mistakes that
-the pins must catch."""
+the token-exact SQuad passes against torch float64 attention with dense token masks and closed
+forms, and planted mistakes that the pins must catch."""
 
 import numpy as np
 import pytest
@@ -76,62 +76,151 @@ def test_window_transpose_groups_positions():
         assert perm[s] % w == s // nw and perm[s] // w == s % nw
 
 
-def _dense_softmax_attention(q, k, v, keep, scale):
-    s = (q @ k.T) * scale
-    s = np.where(keep, s, -np.inf)
-    s -= s.max(axis=1, keepdims=True)
-    p = np.exp(s)
-    return (p / p.sum(axis=1, keepdims=True)) @ v
+def _sdpa_token_mask(q, k, v, keep, scale):
+    """torch float64 scaled_dot_product_attention with a dense boolean token mask, and the LSE of
+    the masked scores (an implementation independent of the oracle's)."""
+    import torch
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    m = torch.from_numpy(keep)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    s = (qt @ kt.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(s.masked_fill(~m, float("-inf")), dim=-1)
+    return o.numpy(), lse.numpy()
 
 
-def test_squad_passes_match_direct_token_attention():
-    """Block-aligned windows, so the local block cover is the token window and the local pass is
-    softmax attention inside each w-token window; the global pass, in the window-transposed order,
-    is the block cover recomputed by hand."""
-    rng = np.random.default_rng(5)
-    n, d, w, bq, bk = 1024, 16, 128, 64, 64   # n / w = 8 tokens per position group
-    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
-    scale = 0.25
-    o, o_local = pt.squad_attention(q, k, v, w, bq, bk, scale)
+def _squad_by_sdpa(q, k, v, w, scale):
+    n = q.shape[-2]
     t = np.arange(n)
-    want_local = _dense_softmax_attention(q[0, 0], k[0, 0], v[0, 0], (t[:, None] // w) == (t[None, :] // w), scale)
-    np.testing.assert_allclose(o_local[0, 0], want_local, rtol=0, atol=1e-12)
-    # global pass: the n / w = 8 tokens of one position group are only 8 apart in the transposed
-    # order, so the block cover (64-token blocks) keeps whole groups together with other groups;
-    # the pin is therefore the block-cover definition, recomputed here by hand
+    local = pt.token_pattern(pt.LOCAL, t[:, None], t[None, :], window=w)
+    glob = pt.token_pattern(pt.GLOBAL, t[:, None], t[None, :], window=w)
+    ol, ll = _sdpa_token_mask(q, k, v, local, scale)
+    og, lg = _sdpa_token_mask(q, k, ol, glob, scale)
+    return og, ol, lg, ll
+
+
+# (n, w): windows that divide n, that do not (a last window of 1 token at 1000 / 37), that are not
+# multiples of any block size, and the degenerate w = 1 and w = n
+SQUAD_CASES = [(1000, 37), (333, 50), (768, 48), (240, 240), (96, 1), (130, 64)]
+
+
+@pytest.mark.parametrize("n,w", SQUAD_CASES)
+def test_squad_matches_token_mask_sdpa(n, w):
+    """Both passes equal softmax attention with the dense token masks of [SQ] "手法": the local
+    pass with floor(t / w) == floor(u / w), the global pass with t mod w == u mod w over the local
+    output as values."""
+    rng = np.random.default_rng(n + w)
+    d = 16
+    q, k, v = (rng.standard_normal((1, 2, n, d)) for _ in range(3))
+    scale = 0.4
+    o, o_local, lse, lse_local = pt.squad_attention(q, k, v, w, scale)
+    ro, rl, rlse, rlse_l = _squad_by_sdpa(q, k, v, w, scale)
+    np.testing.assert_allclose(o_local, rl, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse_local, rlse_l, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+def test_squad_degenerate_windows_are_dense_attention():
+    """w = 1: every token is its own window, so O_local = V exactly and the global pass, where all
+    tokens share position 0, is dense attention over V. w = N: the local pass is dense attention
+    and every token is alone at its position, so O = O_local."""
+    rng = np.random.default_rng(11)
+    n, d = 200, 8
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    dense, dl = _sdpa_token_mask(q, k, v, np.ones((n, n), dtype=bool), 0.5)
+    o, o_local, _, _ = pt.squad_attention(q, k, v, 1, 0.5)
+    assert np.array_equal(o_local, v)
+    np.testing.assert_allclose(o, dense, rtol=0, atol=1e-12)
+    o, o_local, lse, _ = pt.squad_attention(q, k, v, n, 0.5)
+    np.testing.assert_allclose(o_local, dense, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(o, o_local)
+    np.testing.assert_allclose(lse, 0.5 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n,w", [(960, 40), (75600 // 105, 24)])
+def test_squad_global_is_local_in_window_transposed_order(n, w):
+    """Permuting tokens and permuting the outputs back leaves attention unchanged ([SVG2] "2. 手法"
+    A): the global pass equals the local pass with windows of n / w in the window-transposed
+    order, the form the GPU path runs when w divides n."""
+    rng = np.random.default_rng(w)
+    d = 8
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    og, lg = pt.squad_global(q, k, v, w, 0.3)
     perm = pt.window_transpose(n, w)
-    groups = (np.arange(n) // (n // w))
-    keep_perm = (groups[:, None] // (bq // (n // w))) == (groups[None, :] // (bk // (n // w)))
-    gp = _dense_softmax_attention(q[0, 0][perm], k[0, 0][perm], want_local[perm], keep_perm, scale)
-    want = np.empty_like(gp)
-    want[perm] = gp
-    np.testing.assert_allclose(o[0, 0], want, rtol=0, atol=1e-12)
+    op, lp = pt.squad_local(q[..., perm, :], k[..., perm, :], v[..., perm, :], n // w, 0.3)
+    np.testing.assert_allclose(og[..., perm, :], op, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lg[..., perm], lp, rtol=0, atol=1e-13)
 
 
-def test_squad_global_pass_is_same_position_attention_when_groups_fill_blocks():
-    """When n / w equals the block size, each transposed block is exactly one position group, so
-    the global pass is softmax attention among the tokens with the same position in their window."""
-    rng = np.random.default_rng(6)
-    n, d, bq = 64 * 8, 8, 64
-    w = n // bq                                # n / w = 64 = block size
+@pytest.mark.parametrize("n,w", [(100, 7), (96, 12), (75600, 240), (50, 64)])
+def test_squad_pairs(n, w):
+    if n <= 200:
+        t = np.arange(n)
+        want = int(pt.token_pattern(pt.LOCAL, t[:, None], t[None, :], window=w).sum()
+                   + pt.token_pattern(pt.GLOBAL, t[:, None], t[None, :], window=w).sum())
+        assert pt.squad_pairs(n, w) == want
+    if n % w == 0:
+        assert pt.squad_pairs(n, w) == n * w + n * n // w
+
+
+def test_squad_sampled_positions_equal_full():
+    rng = np.random.default_rng(3)
+    n, w, d = 500, 23, 8
     q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
-    o, o_local = pt.squad_attention(q, k, v, w, bq, bq, 0.3)
-    t = np.arange(n)
-    want = _dense_softmax_attention(q[0, 0], k[0, 0], o_local[0, 0], (t[:, None] % w) == (t[None, :] % w), 0.3)
-    np.testing.assert_allclose(o[0, 0], want, rtol=0, atol=1e-12)
+    o, _, _, _ = pt.squad_attention(q, k, v, w, 0.3)
+    pos = [0, 5, 22]
+    os_, _, _, _ = pt.squad_attention(q, k, v, w, 0.3, positions=pos)
+    rows = np.concatenate([np.arange(r, n, w) for r in pos])
+    np.testing.assert_array_equal(os_[..., rows, :], o[..., rows, :])
+    others = np.setdiff1d(np.arange(n), rows)
+    assert np.isnan(os_[..., others, :]).all()
+
+
+def test_squad_planted_mistakes_are_caught(monkeypatch):
+    rng = np.random.default_rng(7)
+    n, w, d, scale = 1000, 37, 8, 0.4
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    ro, rl, _, _ = _squad_by_sdpa(q, k, v, w, scale)
+
+    def err():
+        o, _, _, _ = pt.squad_attention(q, k, v, w, scale)
+        return np.abs(o - ro).max()
+
+    assert err() < 1e-12
+    # the global pass reading V instead of the local output
+    real_global = pt.squad_global
+    monkeypatch.setattr(pt, "squad_global", lambda q_, k_, v_, w_, s_, p_=None: real_global(q_, k_, v, w_, s_, p_))
+    assert err() > 1e-3
+    monkeypatch.undo()
+    # the block cover of the windows (64-token blocks) instead of the token windows
+    real_local = pt.squad_local
+
+    def block_cover_local(q_, k_, v_, w_, s_, windows=None):
+        m = pt.pattern_block_mask(pt.LOCAL, n, 64, 64, window=w_)
+        return oracle.masked_attention(q_, k_, v_, m[None, None], 64, 64, s_)
+    monkeypatch.setattr(pt, "squad_local", block_cover_local)
+    assert err() > 1e-3
+    monkeypatch.setattr(pt, "squad_local", real_local)
+    # same position taken as same window index in the global pass
+    real_attend = pt._attend_set
+    monkeypatch.setattr(pt, "squad_global",
+                        lambda q_, k_, v_, w_, s_, p_=None: real_local(q_, k_, v_, -(-n // w_), s_))
+    assert err() > 1e-3
+    monkeypatch.undo()
+    # a dropped softmax scale
+    monkeypatch.setattr(pt, "_attend_set", lambda a, b, c, s_: real_attend(a, b, c, 1.0))
+    assert err() > 1e-3
 
 
 def test_planted_mistakes_are_caught(monkeypatch):
+    # a transpose that forgets to regroup the positions breaks the transposed-order equivalence
     rng = np.random.default_rng(7)
-    n, d, bq = 64 * 8, 8, 64
-    w = n // bq
-    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
-    o_ok, o_local = pt.squad_attention(q, k, v, w, bq, bq, 0.3)
-    # a transpose that forgets to regroup the positions
-    monkeypatch.setattr(pt, "window_transpose", lambda n_, w_: np.arange(n_))
-    o_bad, _ = pt.squad_attention(q, k, v, w, bq, bq, 0.3)
-    assert np.abs(o_bad - o_ok).max() > 1e-3
-    monkeypatch.undo()
+    n, w = 96, 12
+    q, k, v = (rng.standard_normal((1, 1, n, 8)) for _ in range(3))
+    og, _ = pt.squad_global(q, k, v, w, 0.3)
+    perm = np.arange(n)
+    op, _ = pt.squad_local(q[..., perm, :], k[..., perm, :], v[..., perm, :], n // w, 0.3)
+    assert np.abs(og[..., perm, :] - op).max() > 1e-3
     # a strict band comparison in the diagonal pattern
     real = pt.token_pattern
     monkeypatch.setattr(pt, "token_pattern",
