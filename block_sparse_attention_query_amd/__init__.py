@@ -22,7 +22,7 @@ from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA
 
 __all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
-           "window_transpose", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
+           "window_transpose", "squad_fwd", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
            "probe_workspace_size", "kmeans", "cluster_select", "permute_rows", "cluster_fwd", "svg2_attention",
            "SparseAttnError"]
 
@@ -214,29 +214,49 @@ def window_transpose(x: torch.Tensor, window: int, inverse: bool = False, out: t
 
 
 def squad_masks(B: int, H: int, N: int, window: int, bq: int, bk: int = 64, device="cuda"):
-    """Kept lists of the two SQuad passes: the local pass in raster order and, in the
-    window-transposed order, the local pass over runs of N / window tokens (the global pass)."""
+    """Block covers of the two SQuad token patterns as kept lists (the local windows in raster
+    order; the runs of N / window in the window-transposed order): the tiles the token-exact
+    passes visit, for FLOP accounting and for the block-cover forward of ``fwd_lists``."""
     if window <= 0 or N % window:
         raise ValueError("the window must divide N")
     return (pattern_mask(SA_PAT_LOCAL, B, H, N, bq, bk, window=window, device=device),
             pattern_mask(SA_PAT_LOCAL, B, H, N, bq, bk, window=N // window, device=device))
 
 
-def squad_attention(q, k, v, window: int, bq: int, bk: int = 64, scale: float | None = None, masks=None,
-                    return_local: bool = False):
-    """Two-pass SQuad attention on the block-sparse kernel: O_local = attention with the local
-    mask; then, in the window-transposed token order, attention of (Q, K, O_local) with the global
-    mask, permuted back to raster order. When the kernel can read that order in place (bf16, Bk 64
-    and at least 64 windows), the global pass does so and no transposed copy is made."""
+def squad_fwd(q, k, v, window: int, bq: int, global_pass: bool, scale: float | None = None,
+              out: torch.Tensor | None = None, return_lse: bool = False):
+    """One token-exact SQuad pass (bf16): the local pass (each token attends to its window of
+    ``window`` tokens) or the global pass (each token attends to the tokens at its position
+    inside their windows; ``window`` must divide N and N / window be at least 64)."""
+    _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    ml, mg = squad_masks(B, H, N, window, bq, bk, q.device) if masks is None else masks
-    o_local = fwd_lists(q, k, v, ml["kept_idx"], ml["kept_cnt"], bq, bk, scale)
-    if q.dtype == torch.bfloat16 and bk == 64 and N // window >= 64:
-        o = fwd_lists(q, k, o_local, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale, window=window)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    _lib.check(_lib.lib().sparse_attn_squad_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], B, H, N, d, bq, int(window),
+        _lib.SA_SQUAD_GLOBAL if global_pass else _lib.SA_SQUAD_LOCAL, scale, o.data_ptr(),
+        None if lse is None else lse.data_ptr(), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def squad_attention(q, k, v, window: int, bq: int, bk: int = 64, scale: float | None = None,
+                    return_local: bool = False):
+    """The two-pass SQuad operator, token-exact: O_local = the local pass of (Q, K, V), then the
+    global pass of (Q, K, O_local). The global pass reads the window-transposed order in place
+    when there are at least 64 windows; with fewer it runs as a local pass with windows of
+    N / window over transposed copies (the same arithmetic). ``window`` must divide N."""
+    if bk != 64:
+        raise ValueError("the SQuad passes run on 64-key tiles")
+    B, H, N, d = q.shape
+    if window <= 0 or N % window:
+        raise ValueError("the window must divide N")
+    o_local = squad_fwd(q, k, v, window, bq, False, scale)
+    if N // window >= 64:
+        o = squad_fwd(q, k, o_local, window, bq, True, scale)
     else:
         qt, kt, vt = (window_transpose(t, window) for t in (q, k, o_local))
-        ot = fwd_lists(qt, kt, vt, mg["kept_idx"], mg["kept_cnt"], bq, bk, scale)
-        o = window_transpose(ot, window, inverse=True)
+        o = window_transpose(squad_fwd(qt, kt, vt, N // window, bq, False, scale), window, inverse=True)
     return (o, o_local) if return_local else o
 
 

@@ -14,6 +14,7 @@ SA_ERR_HIP = -3
 SA_BF16 = 0
 SA_F32 = 1
 SA_PAT_LOCAL, SA_PAT_GLOBAL, SA_PAT_DIAG, SA_PAT_MULTIDIAG, SA_PAT_STRIPE = 1, 2, 4, 8, 16
+SA_SQUAD_LOCAL, SA_SQUAD_GLOBAL = 0, 1
 
 # Every symbol include/sparse_attn.h declares, with (restype, argtypes).
 _vp, _i, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
@@ -29,6 +30,7 @@ SIGNATURES = {
                              _vp]),
     "sparse_attn_pattern_mask": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "sparse_attn_window_transpose": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "sparse_attn_squad_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_probe_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "sparse_attn_probe_correct": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _d, _vp, _vp, _vp, _sz,
                                        _vp]),

@@ -23,6 +23,8 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, c
 hipError_t launch_attn_window(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
                               int BH, int N, int d, int Bq, double scale, int window, void* o, float* lse,
                               hipStream_t stream);
+hipError_t launch_attn_squad(const void* q, const void* k, const void* v, int BH, int N, int d, int Bq, double scale,
+                             int window, bool global_pass, void* o, float* lse, hipStream_t stream);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       const uint8_t* mask, int BH, int N, int d, int Bq, double scale, void* dq, void* dk, void* dv,
                       void* ws, hipStream_t stream);
@@ -205,6 +207,27 @@ int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, in
   return hip_status(sa::launch_attn_window(q, k, v, kept_idx, kept_cnt, B * H, N, d, Bq, scale, window, o, lse,
                                            static_cast<hipStream_t>(stream)),
                     "fwd_lists_window: attention launch");
+}
+
+int sparse_attn_squad_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d, int Bq,
+                          int window, int pass, double scale, void* o, float* lse, void* stream) {
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
+  if (rc) return rc;
+  if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "squad_fwd: only SA_BF16 tensors are supported");
+  if (pass != SA_SQUAD_LOCAL && pass != SA_SQUAD_GLOBAL)
+    return fail(SA_ERR_INVALID_ARG, "squad_fwd: pass must be SA_SQUAD_LOCAL or SA_SQUAD_GLOBAL");
+  if (window <= 0 || window > N) return fail(SA_ERR_INVALID_ARG, "squad_fwd: window must be in [1, N]");
+  if (pass == SA_SQUAD_GLOBAL) {
+    if (N % window != 0) return fail(SA_ERR_INVALID_ARG, "squad_fwd: the global pass needs a window that divides N");
+    if ((long long)N * d * 2 > 0xffffffffLL)
+      return fail(SA_ERR_UNSUPPORTED, "squad_fwd: one head's rows (N * d * 2 bytes) must stay below 4 GiB");
+    if (N / window < 64)
+      return fail(SA_ERR_UNSUPPORTED, "squad_fwd: N / window = %d positions per run; at least 64 are needed",
+                  N / window);
+  }
+  return hip_status(sa::launch_attn_squad(q, k, v, B * H, N, d, Bq, scale, window, pass == SA_SQUAD_GLOBAL, o, lse,
+                                          static_cast<hipStream_t>(stream)),
+                    "squad_fwd: attention launch");
 }
 
 int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask, int B, int H, int N,

@@ -349,6 +349,14 @@ __device__ __forceinline__ void dma_tile_wt(const char* __restrict__ base, int k
   }
 }
 
+// K or V block kb into dst: contiguous rows (dma_tile) or rows of the window-transposed order.
+template <int D, int BQ, bool WT>
+__device__ __forceinline__ void copy_tile(const char* __restrict__ base, int kb, int N, int nw, int w, int wave,
+                                          int lane, const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE], lchar* dst) {
+  if constexpr (WT) dma_tile_wt<D, BQ>(base, kb, N, nw, w, wave, off, dst);
+  else dma_tile<D, BQ>(base, kb, N, wave, lane, off, dst);
+}
+
 // ---------------------------------------------------------------- bf16 kernel
 
 // Main loop as a two-stage software pipeline over the kept list. Step t computes the scores of
@@ -362,11 +370,18 @@ __device__ __forceinline__ void dma_tile_wt(const char* __restrict__ base, int k
 // WT: the rows (queries and keys) are those of the window-transposed order (windows of wt_w
 // tokens, wt_nw = N / wt_w >= 64 of them), read from and written to Q, K, V, O and LSE in the
 // original token order.
-template <int D, int BQ, bool WT = false>
+//
+// WIN: no kept lists. Row r attends to exactly the rows of its own window of `win` consecutive
+// rows (windows [c win, (c + 1) win), the last one cut at N), the SQuad local pass; with WT the
+// rows are those of the window-transposed order, where the tokens at one position inside their
+// windows form runs of wt_nw rows, so win = wt_nw gives the SQuad global pass. A query block
+// visits the contiguous range of key blocks that covers its rows' windows, and keys outside a
+// query's window get score -inf element by element.
+template <int D, int BQ, bool WT = false, bool WIN = false>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
-    void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w) {
+    void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w, int win) {
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
@@ -382,10 +397,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31;
   const int hf = lane >> 5;
-  const int cnt = min(max(kcnt[tile], 0), nkb);
+  int cnt, kb_first = 0;
   const int32_t* list = kidx + (size_t)tile * nkb;
+  if constexpr (WIN) {
+    // key blocks from the start of the first row's window to the end of the last row's window
+    const int r0 = qb * BQ, r1 = min(N, r0 + BQ) - 1;
+    const int wend = min(N, (r1 / win + 1) * win);
+    kb_first = (r0 / win) * win / BK;
+    cnt = (wend - 1) / BK - kb_first + 1;
+  } else {
+    cnt = min(max(kcnt[tile], 0), nkb);
+  }
   // list entries are clamped to [0, nKB) so that no load leaves K or V
-  auto blk = [&](int i) { return min(max(list[i], 0), nkb - 1); };
+  auto blk = [&](int i) {
+    if constexpr (WIN) return kb_first + i;
+    else return min(max(list[i], 0), nkb - 1);
+  };
 
   const size_t head_off = (size_t)bh * N * D * 2;
   const char* qbase = static_cast<const char*>(q) + head_off;
@@ -396,8 +423,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   dma_offsets<D, BQ>(wave, lane, doff);
   // K or V block kb into dst: contiguous rows, or rows of the window-transposed order
   auto copy = [&](const char* base, int kb, lchar* dst) {
-    if constexpr (WT) dma_tile_wt<D, BQ>(base, kb, N, wt_nw, wt_w, wave, doff, dst);
-    else dma_tile<D, BQ>(base, kb, N, wave, lane, doff, dst);
+    copy_tile<D, BQ, WT>(base, kb, N, wt_nw, wt_w, wave, lane, doff, dst);
   };
   if (cnt > 0) {
     copy(kbase, blk(0), kb0);
@@ -445,9 +471,25 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   for (int r = 0; r < D / 32; ++r)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[r][i] = 0.f;
-  float m_run = -INFINITY;  // running max in the scaled log2 domain, shared by the lane pair
-  float l_run = 0.f;        // this lane's part of the running sum
+  // running max in the scaled log2 domain, shared by the lane pair. With WIN a query can meet
+  // blocks whose keys all lie outside its window; a finite start keeps exp2(-inf - m) at 0 there
+  // (exp2(-inf + inf) would be undefined), and the first block with a key raises it as before.
+  float m_run = WIN ? -3.0e38f : -INFINITY;
+  float l_run = 0.f;  // this lane's part of the running sum
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // WIN: this lane's query row keeps key rows [wa, wa + wlen); the wave skips the element test
+  // for key blocks inside the one window that holds all of its valid rows
+  int wa = 0, wlen = 0, wv_lo = 1, wv_hi = 0;
+  if constexpr (WIN) {
+    wa = (qrow / win) * win;
+    wlen = max(0, min(win, N - wa));
+    const int w0 = qb * BQ + wave * 32, w1 = min(N, w0 + 32) - 1;
+    if (w0 < N && w0 / win == w1 / win) {
+      wv_lo = (w0 / win) * win;
+      wv_hi = min(N, wv_lo + win);
+    }
+  }
 
   // S^T of the key block in kt (64 keys x 32 queries as two 32 x 32 tiles)
   auto scores = [&](const lchar* kt, f32x16 (&sc)[2]) {
@@ -471,6 +513,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
       if (key >= N) sc[0][i] = -INFINITY;
       if (key + 32 >= N) sc[1][i] = -INFINITY;
+    }
+  };
+  // WIN: keys outside this lane's window (and past N) get score -inf
+  auto mask_win = [&](f32x16 (&sc)[2], int kb) {
+    if (kb * BK >= wv_lo && kb * BK + BK <= wv_hi) return;
+    const int base = kb * BK + 4 * hf - wa;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = base + 8 * (i >> 2) + (i & 3);
+      if ((unsigned)off >= (unsigned)wlen) sc[0][i] = -INFINITY;
+      if ((unsigned)(off + 32) >= (unsigned)wlen) sc[1][i] = -INFINITY;
     }
   };
   // maximum over the block's 64 keys of each query, scaled to the log2 domain
@@ -548,6 +601,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     if constexpr (NEXT != 0) {
       scores(kn, sn);
       if constexpr (NEXT == 2) mask_tail(sn, blk1);
+      if constexpr (WIN) mask_win(sn, blk1);
     }
     if (blk2 >= 0) copy(kbase, blk2, kf);
     if (blk1 >= 0) copy(vbase, blk1, vf);
@@ -564,6 +618,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     __syncthreads();
     scores(kb0, sa);
     if (ragged_last && cnt == 1) mask_tail(sa, blk(0));
+    if constexpr (WIN) mask_win(sa, blk(0));
     raise_max(block_max(sa));
     // steps whose next block is a full one, unrolled by two so that S alternates between sa
     // and sb and the buffers between their even / odd roles without copies
@@ -636,7 +691,7 @@ static hipError_t launch_attn_t(const void* q, const void* k, const void* v, con
                                 float* lse, hipStream_t stream) {
   if constexpr (DT == kBF16) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
-                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0);
+                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0, 0);
   } else {
     hipLaunchKernelGGL((attn_fwd_staged_kernel<DT, D, BQ>), dim3((unsigned)(BH * nqb)), dim3(AttnCfg<DT, D, BQ>::NT),
                        0, stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse);
@@ -675,7 +730,7 @@ hipError_t launch_attn_window(const void* q, const void* k, const void* v, const
 #define SA_WT_CASE(D_, BQ_)                                                                                  \
   if (d == D_ && Bq == BQ_) {                                                                                \
     hipLaunchKernelGGL((attn_fwd_kernel<D_, BQ_, true>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D_, BQ_>::NT), 0, \
-                       stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, nw, window);               \
+                       stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, nw, window, 0);            \
     return hipGetLastError();                                                                                \
   }
   SA_WT_CASE(128, 128)
@@ -683,6 +738,36 @@ hipError_t launch_attn_window(const void* q, const void* k, const void* v, const
   SA_WT_CASE(64, 128)
   SA_WT_CASE(64, 64)
 #undef SA_WT_CASE
+  return hipErrorInvalidValue;
+}
+
+// SQuad passes, token-exact, without lists. WT = false: row t attends to the rows of its window
+// of `window` tokens. WT = true: in the window-transposed order read in place, row s attends to
+// the rows of its run of N / window (the tokens at its position inside their windows).
+template <int D, int BQ, bool WT>
+static hipError_t launch_squad_t(const void* q, const void* k, const void* v, int BH, int N, int nqb, int nkb,
+                                 float c_log2, int window, void* o, float* lse, hipStream_t stream) {
+  const int nw = WT ? N / window : 0;
+  const int32_t* none = nullptr;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BQ, WT, true>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
+                     q, k, v, none, none, N, nqb, nkb, c_log2, o, lse, nw, WT ? window : 0, WT ? nw : window);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_squad(const void* q, const void* k, const void* v, int BH, int N, int d, int Bq, double scale,
+                             int window, bool global_pass, void* o, float* lse, hipStream_t stream) {
+  const int nqb = (N + Bq - 1) / Bq;
+  const int nkb = (N + BK - 1) / BK;
+  const float c_log2 = (float)(scale * 1.4426950408889634);
+#define SA_SQ_CASE(D_, BQ_)                                                                                   \
+  if (d == D_ && Bq == BQ_)                                                                                   \
+    return global_pass ? launch_squad_t<D_, BQ_, true>(q, k, v, BH, N, nqb, nkb, c_log2, window, o, lse, stream) \
+                       : launch_squad_t<D_, BQ_, false>(q, k, v, BH, N, nqb, nkb, c_log2, window, o, lse, stream);
+  SA_SQ_CASE(128, 128)
+  SA_SQ_CASE(128, 64)
+  SA_SQ_CASE(64, 128)
+  SA_SQ_CASE(64, 64)
+#undef SA_SQ_CASE
   return hipErrorInvalidValue;
 }
 

@@ -226,6 +226,32 @@ int sparse_attn_window_transpose(const void* x, int dtype, int B, int H, int N, 
                                  void* out, void* stream);
 
 /*
+ * One pass of the SQuad attention operator, token-exact ([SQuad] "手法", "1. SQuad アテンション・
+ * オペレーター"): every token attends, with a standard softmax, to exactly the key tokens its
+ * rule admits (t a query token, u a key token, w = window):
+ *   pass = SA_SQUAD_LOCAL   floor(t / w) == floor(u / w): the window of w consecutive tokens
+ *                           (the last window is cut at N when w does not divide N);
+ *   pass = SA_SQUAD_GLOBAL  t mod w == u mod w: the tokens at the same position inside their
+ *                           windows, across all windows.
+ * The operator is the local pass of (Q, K, V) followed by the global pass of (Q, K, O_local):
+ * the caller passes the local output as `v` of the global pass. No mask or list is read: a
+ * query block walks the key blocks that cover its rows' windows (the global pass in the
+ * window-transposed order of sparse_attn_window_transpose, read in place) and masks every key
+ * outside a query's own window or position class element by element.
+ *   q, k, v     device, [B, H, N, d] SA_BF16, 16-byte aligned.
+ *   o           device out, [B, H, N, d] SA_BF16 (must not alias q, k or v).
+ *   lse         device out or NULL, [B, H, N] float: natural-log softmax denominators.
+ * Arithmetic as sparse_attn_fwd. Bq in {64, 128}, d in {64, 128}, 1 <= window <= N. The global
+ * pass needs window | N and N / window >= 64 (SA_ERR_UNSUPPORTED otherwise: transpose with
+ * sparse_attn_window_transpose and run the local pass with window N / window instead), and one
+ * head's rows (N * d * 2 bytes) below 4 GiB.
+ */
+#define SA_SQUAD_LOCAL 0
+#define SA_SQUAD_GLOBAL 1
+int sparse_attn_squad_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d, int Bq,
+                          int window, int pass, double scale, void* o, float* lse, void* stream);
+
+/*
  * Bytes of device scratch sparse_attn_probe_correct needs (0 if the sizes are invalid).
  */
 size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int probes);

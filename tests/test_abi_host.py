@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +141,30 @@ def _fwd_lists_window(**kw):
 ])
 def test_fwd_lists_window_rejects(kw, code):
     assert _fwd_lists_window(**kw) == code
+
+
+def _squad(**kw):
+    a = dict(q=P, k=P, v=P, dtype=0, B=1, H=2, N=6400, d=128, Bq=128, window=100, pass_=1, scale=0.125, o=P,
+             lse=None, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_squad_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(v=P_ODD), -1), (dict(dtype=1), -2), (dict(d=48), -2),
+    (dict(Bq=32), -2), (dict(scale=0.0), -1), (dict(pass_=2), -1), (dict(pass_=-1), -1), (dict(window=0), -1),
+    (dict(window=6401), -1), (dict(window=99), -1), (dict(window=128), -2), (dict(N=20_000_000, window=200), -2),
+    (dict(H=0), -1),
+])
+def test_squad_fwd_rejects(kw, code):
+    assert _squad(**kw) == code
+
+
+def test_squad_local_pass_takes_any_window():
+    """The local pass has no divisibility or run-count condition: the same bad-alignment check
+    is what fails first."""
+    assert _squad(pass_=0, window=99, o=P_ODD) == -1
+    assert "aligned" in _lib.lib().sparse_attn_last_error().decode()
 
 
 def test_last_error_names_the_problem():

@@ -138,6 +138,35 @@ def test_squad_attention_matches_oracle(n, w, d, bq):
     assert e.max() <= O_MAX and e.mean() <= O_MEAN
 
 
+@pytest.mark.parametrize("n,w,d,bq", [(4800, 75, 128, 128), (6400, 100, 64, 64), (75600, 240, 128, 128)])
+def test_squad_global_in_place_is_the_transposed_local_pass(n, w, d, bq):
+    """The global pass read in place equals, bit for bit, the local pass with windows of n / w over
+    window-transposed copies of Q, K and V, transposed back (O and LSE)."""
+    H = 1 if n > 10000 else 2
+    g = torch.Generator().manual_seed(n - w)
+    q, k, v = (torch.randn(1, H, n, d, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3))
+    o, lse = sa.squad_fwd(q, k, v, w, bq, True, return_lse=True)
+    qt, kt, vt = (sa.window_transpose(t, w) for t in (q, k, v))
+    ot, lt = sa.squad_fwd(qt, kt, vt, n // w, bq, False, return_lse=True)
+    perm = torch.from_numpy(pt.window_transpose(n, w)).to(DEV)
+    ref_lse = torch.empty_like(lt)
+    ref_lse[:, :, perm] = lt
+    assert torch.equal(o, sa.window_transpose(ot, w, inverse=True))
+    assert torch.equal(lse, ref_lse)
+
+
+def test_squad_lse_matches_oracle():
+    """LSE of both passes against the oracle, within the bf16 rounding of P (ln(1 + 2^-8))."""
+    n, w, d, bq = 7680, 120, 128, 64   # 64 windows: the global pass runs in place
+    g = torch.Generator().manual_seed(21)
+    q, k, v = (torch.randn(1, 2, n, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    ol, ll = sa.squad_fwd(q.to(DEV), k.to(DEV), v.to(DEV), w, bq, False, return_lse=True)
+    _, lg = sa.squad_fwd(q.to(DEV), k.to(DEV), ol, w, bq, True, return_lse=True)
+    _, rl, rlse, rlse_l = pt.squad_attention(f64(q), f64(k), f64(v), w, 1.0 / math.sqrt(d))
+    assert np.all(np.abs(f64(ll) - rlse_l) <= 1e-3 + math.log1p(2.0 ** -8))
+    assert np.all(np.abs(f64(lg) - rlse) <= 1e-3 + math.log1p(2.0 ** -8))
+
+
 def test_vdit_pattern_attention_matches_oracle():
     """Sparse-vDiT style union (diagonal band, the same band every `period` tokens, and the first
     key token of each period) through sparse_attn_fwd."""
