@@ -50,8 +50,9 @@ extern "C" {
 #define SA_ERR_UNSUPPORTED (-2) /* d, Bq, Bk, dtype or nKB outside the instantiated set    */
 #define SA_ERR_HIP (-3)         /* a HIP launch failed; the HIP message is kept          */
 
-/* Element types of Q, K, V and O. Both are computed with bf16 MFMA operands and fp32
- * accumulation; fp32 tiles are rounded to bf16 (nearest-even) when staged. */
+/* Element types of Q, K, V and O. SA_BF16 attention runs on bf16 MFMA operands (P rounded to
+ * bf16 for the P V product) with fp32 accumulation; SA_F32 attention runs on the fp32 matrix
+ * instruction with fp32 P, so no fp32 input is rounded. */
 #define SA_BF16 0
 #define SA_F32 1
 
@@ -117,7 +118,8 @@ size_t sparse_attn_fwd_workspace_size(int B, int H, int N, int Bq, int Bk);
  *   workspace   device scratch of at least sparse_attn_fwd_workspace_size() bytes, 256-byte
  *               aligned; overwritten.
  * The mask is compacted into ascending kept-block lists in the workspace, then one workgroup
- * per (b, h, query block) walks its list with bf16 MFMA and an fp32 online softmax.
+ * per (b, h, query block) walks its list with bf16 (or, for SA_F32, fp32) MFMA and an fp32
+ * online softmax.
  */
 int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
                     int B, int H, int N, int d, int Bq, int Bk, double scale, void* o, float* lse,
