@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA_PAT_MULTIDIAG,  # noqa: F401
                    SA_PAT_STRIPE, SparseAttnError)
 
-__all__ = ["pool_qk", "select_mask", "fwd", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
+__all__ = ["pool_qk", "select_mask", "fwd", "fwd_noalloc", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
            "window_transpose", "squad_fwd", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
            "probe_workspace_size", "kmeans", "cluster_select", "permute_rows", "cluster_fwd", "svg2_attention",
@@ -140,6 +140,27 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, b
                                           None if lse is None else lse.data_ptr(), workspace.data_ptr(),
                                           workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if return_lse else o
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor, bq: int, bk: int = 64,
+                scale: float | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """``fwd`` through the entry point that allocates nothing on the device (its kept lists live
+    in a scratch array inside the library). Pass ``out`` (and ``lse``) to allocate nothing here
+    either; returns (o, lse)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (B, H, nqb, nkb) or not mask.is_contiguous() \
+            or mask.device != q.device:
+        raise ValueError(f"mask must be a contiguous uint8 [{B}, {H}, {nqb}, {nkb}] tensor on {q.device}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_out(lse, (B, H, N), torch.float32, q.device)
+    _lib.check(_lib.lib().sparse_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype],
+                                                  mask.data_ptr(), B, H, N, d, bq, bk, scale, o.data_ptr(),
+                                                  None if lse is None else lse.data_ptr(), _stream(q)))
+    return o, lse
 
 
 def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor, kept_cnt: torch.Tensor,

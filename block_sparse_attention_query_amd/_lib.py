@@ -15,6 +15,7 @@ SA_BF16 = 0
 SA_F32 = 1
 SA_PAT_LOCAL, SA_PAT_GLOBAL, SA_PAT_DIAG, SA_PAT_MULTIDIAG, SA_PAT_STRIPE = 1, 2, 4, 8, 16
 SA_SQUAD_LOCAL, SA_SQUAD_GLOBAL = 0, 1
+SA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/sparse_attn.h declares, with (restype, argtypes).
 _vp, _i, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
@@ -23,6 +24,7 @@ SIGNATURES = {
     "sparse_attn_select_mask": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _d, _d, _d, _vp, _vp, _vp, _vp, _vp]),
     "sparse_attn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_fwd": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp, _sz, _vp]),
+    "sparse_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_fwd_lists": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_fwd_lists_window": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),

@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/sparse_attn.h"
 
 namespace sa {
@@ -207,6 +209,83 @@ int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, in
   return hip_status(sa::launch_attn_window(q, k, v, kept_idx, kept_cnt, B * H, N, d, Bq, scale, window, o, lse,
                                            static_cast<hipStream_t>(stream)),
                     "fwd_lists_window: attention launch");
+}
+
+}  // extern "C"
+
+// Scratch of sparse_attn_fwd_noalloc: the kept lists and counts of a group of heads. Every GPU the
+// library runs on holds its own copy until the process ends. Host code must not use this name as
+// an address (it is a host-side stand-in): the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_ERR_UNSUPPORTED, "fwd_noalloc: device %d is beyond the %d devices tracked", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "fwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(SA_ERR_HIP, "fwd_noalloc: hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask, int B, int H,
+                            int N, int d, int Bq, int Bk, double scale, void* o, float* lse, void* stream) {
+  if (!mask) return fail(SA_ERR_INVALID_ARG, "fwd_noalloc: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, o);
+  if (rc) return rc;
+  const int nqb = cdiv(N, Bq), nkb = cdiv(N, Bk);
+  // one head's lists and counts, each rounded up to the 256-byte alignment of a group's arrays
+  const size_t head_bytes = align_up((size_t)nqb * nkb * sizeof(int32_t)) + align_up((size_t)nqb * sizeof(int32_t));
+  if (head_bytes > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+    return fail(SA_ERR_UNSUPPORTED, "fwd_noalloc: one head's kept lists need %zu bytes; the scratch holds %zu",
+                head_bytes, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  const int BH = B * H;
+  const int group = (int)((size_t)SA_NOALLOC_SCRATCH_BYTES / head_bytes < (size_t)BH
+                              ? (size_t)SA_NOALLOC_SCRATCH_BYTES / head_bytes
+                              : (size_t)BH);
+  const size_t es = dtype == SA_BF16 ? 2 : 4;
+  const size_t head_elems = (size_t)N * d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // groups of heads run one after another on the stream, so each reuses the scratch after the
+  // previous group's attention has read it
+  for (int h0 = 0; h0 < BH; h0 += group) {
+    const int g = BH - h0 < group ? BH - h0 : group;
+    int32_t* kidx = static_cast<int32_t*>(ws);
+    int32_t* kcnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                               align_up((size_t)g * nqb * nkb * sizeof(int32_t)));
+    const size_t off = (size_t)h0 * head_elems * es;
+    rc = hip_status(sa::launch_compact(mask + (size_t)h0 * nqb * nkb, g * nqb, nkb, kidx, kcnt, s),
+                    "fwd_noalloc: compaction launch");
+    if (rc) return rc;
+    rc = hip_status(sa::launch_attn(static_cast<const char*>(q) + off, static_cast<const char*>(k) + off,
+                                    static_cast<const char*>(v) + off, dtype, kidx, kcnt, g, N, d, Bq, scale,
+                                    static_cast<char*>(o) + off, lse ? lse + (size_t)h0 * N : nullptr, s),
+                    "fwd_noalloc: attention launch");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 int sparse_attn_squad_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H, int N, int d, int Bq,

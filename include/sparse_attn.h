@@ -126,6 +126,22 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, cons
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sparse_attn_fwd without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The kept lists go to
+ * a scratch array inside the library (SA_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends); heads are processed in groups whose lists fit in it, one group after another on
+ * `stream`. The call itself allocates nothing. Arguments, arithmetic and results are those of
+ * sparse_attn_fwd (bit-identical outputs).
+ * Limit: one head's lists, align256(nQB * nKB * 4) + align256(nQB * 4) bytes, must fit in the
+ * scratch (SA_ERR_UNSUPPORTED otherwise; e.g. N = 75600, Bq = 128, Bk = 64 needs 2.8 MB).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or threads without ordering) race and give unspecified results.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask, int B, int H,
+                            int N, int d, int Bq, int Bk, double scale, void* o, float* lse, void* stream);
+
+/*
  * The same attention from kept-block lists instead of a mask (the kept_idx / kept_cnt that
  * sparse_attn_select_mask can write), skipping the compaction step.
  *

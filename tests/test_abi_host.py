@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +141,29 @@ def _fwd_lists_window(**kw):
 ])
 def test_fwd_lists_window_rejects(kw, code):
     assert _fwd_lists_window(**kw) == code
+
+
+def _fwd_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, dtype=0, mask=P, B=1, H=2, N=1000, d=128, Bq=128, Bk=64, scale=0.125, o=P, lse=None,
+             stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_fwd_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), -1), (dict(q=None), -1), (dict(o=P_ODD), -1), (dict(d=48), -2), (dict(Bq=32), -2),
+    (dict(Bk=128), -2), (dict(dtype=2), -2), (dict(scale=-1.0), -1), (dict(N=0), -1),
+    # one head's lists (4096 x 8192 int32 = 128 MiB) exceed the 32 MiB scratch: rejected before any HIP call
+    (dict(N=524288), -2),
+])
+def test_fwd_noalloc_rejects(kw, code):
+    assert _fwd_noalloc(**kw) == code
+
+
+def test_fwd_noalloc_names_the_scratch_limit():
+    assert _fwd_noalloc(N=300000) == -2
+    msg = _lib.lib().sparse_attn_last_error().decode()
+    assert "scratch" in msg and str(_lib.SA_NOALLOC_SCRATCH_BYTES) in msg
 
 
 def _squad(**kw):
