@@ -215,7 +215,7 @@ template <int D, int BQ, bool WT>
 __device__ __forceinline__ void copy_tile(const char* __restrict__ base, int kb, int N, int nw, int w, int wave,
                                           int lane, const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE], lchar* dst) {
   if constexpr (WT) dma_tile_wt<D, BQ>(base, kb, N, nw, w, wave, off, dst);
-  else dma_tile<D, BQ>(base, kb, N, wave, lane, off, dst);
+  else dma_tile_rsrc<D, BQ>(base, kb, N, wave, off, dst);
 }
 
 // ---------------------------------------------------------------- bf16 kernel

@@ -88,4 +88,26 @@ __device__ __forceinline__ void dma_tile(const char* __restrict__ base, int kb, 
   }
 }
 
+// dma_tile through a buffer resource: the descriptor covers the rows from key block kb to the end
+// of the head (uniform, built in SGPRs), each lane adds its constant 32-bit offset, and rows past
+// N lie outside the descriptor's range, so the hardware reads them as zeros instead of the copy
+// clamping them. No per-lane address arithmetic. One head's rows must stay below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* __restrict__ base, int kb, int N,
+                                                            int rowb) {
+  const int first = kb * BK;
+  const int bytes = max(0, N - first) * rowb;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (size_t)first * rowb, (short)0, bytes,
+                                           0x00020000);
+}
+
+template <int D, int BQ>
+__device__ __forceinline__ void dma_tile_rsrc(const char* __restrict__ base, int kb, int N, int wave,
+                                              const uint32_t (&off)[DCfg<D, BQ>::PER_WAVE], lchar* dst) {
+  using C = DCfg<D, BQ>;
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, kb, N, C::ROWB);
+#pragma unroll
+  for (int u = 0; u < C::PER_WAVE; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + (wave * C::PER_WAVE + u) * 1024, 16, off[u], 0, 0, 0);
+}
+
 }  // namespace sa
