@@ -450,6 +450,72 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const bool ragged_last = cnt > 0 && (N % BK) != 0 && blk(cnt - 1) == nkb - 1;
   // Step t. NEXT: 0 = no block t + 1 (last step), 1 = full block t + 1, 2 = ragged block t + 1.
   // kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1).
+  // Word j (0..15) of P^T packed to bf16: tile h = j & 1, elements 8 u + 2 e and 8 u + 2 e + 1 with
+  // u = j >> 3, e = (j >> 1) & 3; the row sum takes the same bf16 values, into partial sum
+  // (e & 1) * 2 + h (the order of the adds is that of accumulate).
+  auto p_word = [&](const f32x16 (&sc)[2], int j, uint32_t (&pw)[16], float (&rs)[4]) {
+    const int h = j & 1, u = j >> 3, e = (j >> 1) & 3;
+    pw[j] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[h][8 * u + 2 * e], c_log2, -m_run)),
+                      __builtin_amdgcn_exp2f(fmaf(sc[h][8 * u + 2 * e + 1], c_log2, -m_run)));
+    // an empty asm on the word keeps its exps here: IR passes would otherwise sink them to the P V
+    // products, past the scheduling fences
+    asm volatile("" : "+v"(pw[j]));
+    rs[(e & 1) * 2 + h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]), ones,
+                                                          rs[(e & 1) * 2 + h], false);
+  };
+  // O^T += V^T P^T for the packed words of the block in vt
+  auto pv = [&](const uint32_t (&pw)[16], lchar* vt) {
+    bf16x8 pb[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u], pw[8 * u + 2], pw[8 * u + 4], pw[8 * u + 6]));
+      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u + 1], pw[8 * u + 3], pw[8 * u + 5], pw[8 * u + 7]));
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
+        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
+      }
+  };
+  // S^T of the key block in kt into sn, interleaved with the P words of sc: each pair of score
+  // MFMAs is followed by two P words, and the K fragments are read two steps ahead (three slots),
+  // so the vector units and the LDS reads run under the matrix products of one wave.
+  auto scores_p = [&](const lchar* kt, f32x16 (&sn)[2], const f32x16 (&sc)[2], uint32_t (&pw)[16],
+                      float (&rs)[4]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sn[0][i] = 0.f;
+      sn[1][i] = 0.f;
+    }
+    bf16x8 a0[3], a1[3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      a0[s] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s]);
+      a1[s] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s] + 32 * C::ROWB);
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      if (s + 2 < D / 16) {
+        a0[(s + 2) % 3] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s + 2]);
+        a1[(s + 2) % 3] =
+            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s + 2] + 32 * C::ROWB);
+      }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s % 3], qf[s], sn[0], 0, 0, 0);
+      if (2 * s < 16) p_word(sc, 2 * s, pw, rs);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s % 3], qf[s], sn[1], 0, 0, 0);
+      if (2 * s + 1 < 16) p_word(sc, 2 * s + 1, pw, rs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 2 * (D / 16); j < 16; ++j) p_word(sc, j, pw, rs);
+  };
+
   auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
                   auto next_tag) {
     constexpr int NEXT = decltype(next_tag)::value;
@@ -459,14 +525,20 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     // by the barrier start on the matrix cores instead of queueing their copies first
     const int blk2 = t + 2 < cnt ? blk(t + 2) : -1;
     const int blk1 = t + 1 < cnt ? blk(t + 1) : -1;
+    uint32_t pw[16];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (NEXT != 0) {
-      scores(kn, sn);
+      scores_p(kn, sn, sc, pw, rs);
       if constexpr (NEXT == 2) mask_tail(sn, blk1);
       if constexpr (WIN) mask_win(sn, blk1);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p_word(sc, j, pw, rs);
     }
     if (blk2 >= 0) copy(kbase, blk2, kf);
     if (blk1 >= 0) copy(vbase, blk1, vf);
-    accumulate(sc, vc);
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    pv(pw, vc);
     if constexpr (NEXT != 0) raise_max(block_max(sn));
   };
 
