@@ -166,3 +166,45 @@ def test_error_scales_bound_the_gradients():
     part = bw.masked_attention_bwd_scales(q, k, v, mask, g, bq, bk, q_blocks=[(0, 1, 1)], k_blocks=[(0, 0, 2)])
     np.testing.assert_allclose(part[0][0, 1, 32:64], scales[0][0, 1, 32:64], atol=1e-13)
     np.testing.assert_allclose(part[1][0, 0, 32:48], scales[1][0, 0, 32:48], atol=1e-13)
+
+
+def test_error_scales_closed_form_one_key():
+    """One query attending to one key: P = 1 and O = V, so dP = D = dO.V and dS = 0. The gradients
+    are dQ = dK = 0 and dV = dO; the scales reduce exactly to the D-spread term for dQ and dK,
+    scale * e |K| and scale * e |Q| with e = sum_c |dO_c V_c|, and to |dO| for dV. Equality pins
+    the scale function from both sides: a dropped D term gives zero, a doubled term twice the
+    value."""
+    rng = np.random.default_rng(41)
+    d, sc = 8, 0.3
+    q, k, v, g = (rng.standard_normal((1, 1, 1, d)) for _ in range(4))
+    mask = np.ones((1, 1, 1, 1), dtype=np.uint8)
+    dq, dk, dv = bw.masked_attention_bwd(q, k, v, mask, g, 1, 1, sc)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    np.testing.assert_allclose(dv, g, rtol=0, atol=1e-15)
+    sq, sk, sv = bw.masked_attention_bwd_scales(q, k, v, mask, g, 1, 1, sc)
+    e = np.abs(g * v).sum()
+    np.testing.assert_allclose(sq, sc * e * np.abs(k), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(sk, sc * e * np.abs(q), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(sv, np.abs(g), rtol=1e-14, atol=0)
+
+
+def test_error_scales_closed_form_two_tied_keys():
+    """Two identical queries (same dO) and two identical keys: for each query P = (1/2, 1/2),
+    O = (V_1 + V_2) / 2, dP_u = dO.V_u, D = (dP_1 + dP_2) / 2, so |dS_1| = |dS_2| = |dP_1 - dP_2| / 4.
+    With e = sum_c |dO_c O_c|: scale(dQ_t) = scale (|dS_1| + e / 2) (|K_1| + |K_2|) for each query,
+    and over the two queries scale(dK_u) = 2 scale (|dS_1| + e / 2) |Q| and scale(dV_u) = |dO|."""
+    rng = np.random.default_rng(42)
+    d, sc = 6, 0.7
+    q0, k1, g0 = (rng.standard_normal(d) for _ in range(3))
+    q = np.stack([q0, q0])[None, None]
+    k = np.stack([k1, k1])[None, None]
+    g = np.stack([g0, g0])[None, None]
+    v = rng.standard_normal((1, 1, 2, d))
+    mask = np.ones((1, 1, 1, 1), dtype=np.uint8)
+    sq, sk, sv = bw.masked_attention_bwd_scales(q, k, v, mask, g, 2, 2, sc)
+    dp = v[0, 0] @ g0
+    ds1 = abs(dp[0] - dp[1]) / 4
+    e = np.abs(g0 * (v[0, 0, 0] + v[0, 0, 1]) / 2).sum()
+    np.testing.assert_allclose(sq[0, 0], np.stack([sc * (ds1 + e / 2) * 2 * np.abs(k1)] * 2), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(sk[0, 0], np.stack([2 * sc * (ds1 + e / 2) * np.abs(q0)] * 2), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(sv[0, 0], np.stack([np.abs(g0)] * 2), rtol=1e-13, atol=0)
