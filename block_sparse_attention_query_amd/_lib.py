@@ -6,6 +6,8 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
+# The host tests can point this module at another build of the same ABI (the sanitizer build).
+LIB_PATH = os.environ.get("SA_LIB_PATH", LIB_PATH)
 
 SA_OK = 0
 SA_ERR_INVALID_ARG = -1

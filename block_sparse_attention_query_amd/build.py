@@ -52,5 +52,41 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side sanitizer build of the C ABI's argument checks: api.cpp's host code compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer (its device pass is unchanged), linked with the
+# regular objects of the other sources. Run on the CPU only, with the sanitizer runtime preloaded
+# (the CPU test suite does this for the host ABI tests).
+CLANGXX = "/opt/rocm/lib/llvm/bin/clang++"
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise FileNotFoundError("clang AddressSanitizer runtime not found")
+    return hits[-1]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    os.makedirs(out_dir, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, [s for s in SOURCES if s != "api.cpp"]))
+    api_obj = os.path.join(out_dir, "api_san.o")
+    cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, *SANITIZE_HOST, "-g", "-c", os.path.join(CSRC, "api.cpp"),
+           "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    out = os.path.join(out_dir, "libsparse_attn_hostsan.so")
+    cmd = [CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", api_obj, *objs,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build()

@@ -9,9 +9,22 @@ import re
 import pytest
 
 import oracle
-from block_sparse_attention_query_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_lib_module():
+    """The ctypes table (_lib.py) loaded by path, without the package's torch binding, so these
+    tests also run under a preloaded sanitizer runtime."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "sa_abi_lib", os.path.join(ROOT, "block_sparse_attention_query_amd", "_lib.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_lib = _load_lib_module()
 HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsparse_attn.so not built")

@@ -10,7 +10,7 @@ e = sum |dO O|, spread to dS by P). The fp32 accumulation adds orders of magnitu
 |err| <= 4u times the elementwise scale of masked_attention_bwd_scales (the products over
 absolute values plus the D term), for each of dQ, dK, dV: the max bar. The mean bar is u times
 the mean scale (rounding errors of independent terms do not all line up).
-""""""
+"""
 
 import math
 
