@@ -26,6 +26,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan720p_traffic.json")
+WORKLOAD_SHAPES = {"wan720p": "Wan2.1-14B 720p-shaped", "wan480p": "Wan2.1-1.3B 480p-shaped",
+                   "stress": "distribution stress (near-uniform and sink-skewed heads),", "tiny": "tiny fp32",
+                   "sweep720p": "Wan2.1-14B 720p-shaped"}
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_query_amd", "csrc", f)
                 for f in ("attn_fwd.hip", "attn_tiles.h", "sa_common.h")]
 
@@ -582,7 +585,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: Wan2.1-14B 720p-shaped latent grid 21x45x80",
+        "config": {"workload": f"{w.name}: {WORKLOAD_SHAPES.get(w.name, 'synthetic')} latent grid "
+                               f"{w.grid[0]}x{w.grid[1]}x{w.grid[2]}",
                    "batch": B, "heads": H, "tokens": N, "head_dim": d, "bq": w.bq, "bk": w.bk,
                    "k_frac": w.k_frac, "p": w.p, "kept_block_density": round(density, 5),
                    "block_sparsity": round(1 - density, 5), "executed_tflop_per_step": round(flops / 1e12, 4),
