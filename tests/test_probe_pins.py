@@ -103,3 +103,80 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(pr, "fit_correction", mutant)
     with pytest.raises(AssertionError):
         test_affine_residual_is_recovered()
+
+
+def _rank_case(seed, m=200, d=12, k=5, noise=0.05):
+    """Probe rows whose residual has k dominant directions (singular values 8..4) plus noise."""
+    rng = np.random.default_rng(seed)
+    xs = rng.standard_normal((1, 1, m, d))
+    u = np.linalg.qr(rng.standard_normal((m, k)))[0]
+    w = np.linalg.qr(rng.standard_normal((d, k)))[0]
+    r = u @ np.diag(np.linspace(8, 4, k)) @ w.T + noise * rng.standard_normal((m, d))
+    return xs, xs + r[None, None], r
+
+
+def test_full_rank_is_the_unprojected_fit():
+    xs, xe, _ = _rank_case(11)
+    d = xs.shape[-1]
+    np.testing.assert_allclose(pr.fit_correction(xs, xe, 1e-3, rank=d), pr.fit_correction(xs, xe, 1e-3),
+                               rtol=0, atol=1e-13)
+
+
+def test_exactly_low_rank_residual_is_left_unchanged():
+    """A residual of exact rank k: the unprojected map's rows already lie in its row space, so
+    any rank >= k reproduces it."""
+    xs, xe, _ = _rank_case(12, noise=0.0)
+    full = pr.fit_correction(xs, xe, 1e-3)
+    for r in (5, 7, 11):
+        np.testing.assert_allclose(pr.fit_correction(xs, xe, 1e-3, rank=r), full, rtol=0, atol=1e-11)
+    assert np.abs(pr.fit_correction(xs, xe, 1e-3, rank=3) - full).max() > 1e-3
+
+
+def test_correction_rows_lie_in_top_singular_subspace():
+    """Every correction row [O, 1] A lies in the span of the top-r right singular vectors of R,
+    computed here by the SVD of R (a different routine from the oracle's eigendecomposition of
+    R^T R), and the captured energy |R V_r|^2 is the sum of the r largest squared singular values
+    (Eckart-Young)."""
+    xs, xe, r = _rank_case(13)
+    _, sv, wt = np.linalg.svd(r)
+    for rank in (1, 3, 5):
+        a = pr.fit_correction(xs, xe, 1e-3, rank=rank)
+        basis = wt[:rank].T
+        rows = np.concatenate([xs[0, 0], np.ones((xs.shape[2], 1))], axis=1) @ a[0, 0]
+        np.testing.assert_allclose(rows - rows @ basis @ basis.T, 0.0, atol=1e-10)
+        vr = pr.residual_subspace(r, rank)
+        np.testing.assert_allclose(np.linalg.norm(r @ vr) ** 2, (sv[:rank] ** 2).sum(), rtol=1e-12)
+        np.testing.assert_allclose(vr.T @ vr, np.eye(rank), atol=1e-12)
+
+
+def test_rank_one_residual_closed_form():
+    """R = u w^T: the subspace is the line of w, and with rank 1 the map is A_full w w^T / |w|^2."""
+    rng = np.random.default_rng(14)
+    m, d = 80, 6
+    xs = rng.standard_normal((1, 1, m, d))
+    u, w = rng.standard_normal(m), rng.standard_normal(d)
+    xe = xs + np.outer(u, w)[None, None]
+    full = pr.fit_correction(xs, xe, 1e-3)
+    np.testing.assert_allclose(pr.fit_correction(xs, xe, 1e-3, rank=1), full @ np.outer(w, w) / (w @ w), atol=1e-12)
+
+
+def _subspace_smallest(r, rank):
+    evals, evecs = np.linalg.eigh(np.asarray(r, dtype=np.float64).T @ np.asarray(r, dtype=np.float64))
+    return evecs[:, :rank]
+
+
+_REAL_FIT_R = pr.fit_correction
+
+
+def _fit_projection_dropped(xs, xe, ridge, rank=None):
+    return _REAL_FIT_R(xs, xe, ridge, None)
+
+
+@pytest.mark.parametrize("mutant", ["smallest", "dropped"])
+def test_subspace_planted_mistakes_are_caught(monkeypatch, mutant):
+    if mutant == "smallest":
+        monkeypatch.setattr(pr, "residual_subspace", _subspace_smallest)
+    else:
+        monkeypatch.setattr(pr, "fit_correction", _fit_projection_dropped)
+    with pytest.raises(AssertionError):
+        test_correction_rows_lie_in_top_singular_subspace()
