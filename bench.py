@@ -284,7 +284,7 @@ def corrected_bench(args, sa, w, q, k, v, gen_s):
         sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, out=o)
         if ev is not None:
             ev[2].record()
-        sa.probe_correct(q, k, v, o, w.bq, P, ridge, workspace=ws)
+        sa.probe_correct(q, k, v, o, w.bq, P, ridge, workspace=ws, rank=args.rank)
         if ev is not None:
             ev[3].record()
 
@@ -319,6 +319,11 @@ def corrected_bench(args, sa, w, q, k, v, gen_s):
     rows = torch.cat([torch.arange(i * w.bq, min(N, (i + 1) * w.bq)) for i in held]).to(q.device)
     ex, sp, co = (t[:, :, rows].float() for t in (o_ex, o_s, o))
     rel = lambda t: float((t - ex).norm() / ex.norm())  # noqa: E731
+    by_rank = {}
+    for r in args.rank_sweep:  # untimed: the same correction confined to r principal directions
+        o_r = o_s.clone()
+        sa.probe_correct(q, k, v, o_r, w.bq, P, ridge, workspace=ws, rank=r)
+        by_rank[str(r)] = round(rel(o_r[:, :, rows].float()), 5)
     tflops = flops / (ms * 1e-3) / 1e12
     return {
         "metric": "sparse attention fwd + probe-fitted correction TFLOP/s (executed)",
@@ -327,14 +332,15 @@ def corrected_bench(args, sa, w, q, k, v, gen_s):
         "dtype": "bf16", "data": "synthetic" + (", smooth values" if args.smooth_v else ""),
         "config": {"workload": f"{w.name}: hybrid mask, then {P} probe blocks per head", "batch": B, "heads": H,
                    "tokens": N, "head_dim": d, "bq": w.bq, "bk": w.bk, "k_frac": w.k_frac, "p": w.p,
-                   "probes": P, "ridge": ridge, "kept_block_density": round(float(mask_cpu.mean()), 5),
+                   "probes": P, "ridge": ridge, "rank": d if args.rank is None else args.rank,
+                   "kept_block_density": round(float(mask_cpu.mean()), 5),
                    "executed_tflop_per_step": round(flops / 1e12, 4),
                    "probe_dense_tflop": round(probe_flops / 1e12, 4), "apply_tflop": round(apply_flops / 1e12, 4),
                    "parallelism": "none (1 GPU)"},
         "ms_per_call": {"pool_qk+select_mask": round(mask_ms, 4), "fwd_lists": round(attn_ms, 4),
                         "probe_correct": round(corr_ms, 4)},
         "heldout_rel_l2_error": {"query_blocks_per_head": len(held), "sparse": round(rel(sp), 5),
-                                 "corrected": round(rel(co), 5)},
+                                 "corrected": round(rel(co), 5), "corrected_by_rank": by_rank},
         "roofline": {"kernel": "attn_fwd_kernel<bf16, 128, 128>", "bound": "mfma",
                      "achieved": round(executed_flops(mask_cpu, N, w.bq, w.bk, d) / (attn_ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -462,6 +468,11 @@ def main(argv=None):
     ap.add_argument("--correct", type=int, default=0, metavar="PROBES",
                     help="time the hot path followed by the probe-fitted residual correction with PROBES probe "
                          "query blocks per head (ridge 1e-3), and report held-out error before and after")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="--correct: confine the map to RANK principal directions of the probe residuals "
+                         "(default: head_dim, no limit)")
+    ap.add_argument("--rank-sweep", type=lambda t: [int(x) for x in t.split(",") if x], default=[],
+                    help="--correct: also report the held-out error for these comma-separated ranks (untimed)")
     ap.add_argument("--svg2", action="store_true",
                     help="time the semantic-aware permutation path (k-means clusters, centroid Top-p, attention "
                          "over variable-size blocks) instead of the block-mask path")

@@ -319,8 +319,9 @@ def probe_workspace_size(B: int, H: int, N: int, d: int, bq: int, probes: int) -
 
 
 def probe_correct(q, k, v, o, bq: int, probes: int, ridge: float, scale: float | None = None,
-                  workspace: torch.Tensor | None = None, return_fit: bool = False):
-    """Probe-fitted residual correction of the sparse output ``o`` (bf16), in place.
+                  workspace: torch.Tensor | None = None, return_fit: bool = False, rank: int | None = None):
+    """Probe-fitted residual correction of the sparse output ``o`` (bf16), in place. ``rank``
+    confines the map to that many principal directions of the probe residuals (None: no limit).
 
     With ``return_fit`` also returns A (float32 ``[B, H, d + 1, d]``) and the exact probe rows
     (float32 ``[B, H, probes * bq, d]``)."""
@@ -334,7 +335,8 @@ def probe_correct(q, k, v, o, bq: int, probes: int, ridge: float, scale: float |
         exact = torch.empty((B, H, probes * bq, d), dtype=torch.float32, device=q.device)
     _lib.check(_lib.lib().sparse_attn_probe_correct(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _DTYPES[q.dtype], B, H, N, d, bq, scale, int(probes),
-        float(ridge), a.data_ptr() if a is not None else None, exact.data_ptr() if exact is not None else None,
+        float(ridge), d if rank is None else int(rank), a.data_ptr() if a is not None else None,
+        exact.data_ptr() if exact is not None else None,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, a, exact) if return_fit else o
 

@@ -36,8 +36,8 @@ SIGNATURES = {
     "sparse_attn_window_transpose": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "sparse_attn_squad_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_probe_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "sparse_attn_probe_correct": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _d, _vp, _vp, _vp, _sz,
-                                       _vp]),
+    "sparse_attn_probe_correct": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _i, _d, _i, _vp, _vp, _vp,
+                                       _sz, _vp]),
     "sparse_attn_kmeans_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_kmeans": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sparse_attn_cluster_select": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _d, _d, _vp, _vp, _vp]),

@@ -37,7 +37,7 @@ hipError_t launch_window_transpose(const void* x, void* out, int BH, int N, int 
                                    hipStream_t stream);
 size_t probe_workspace_bytes(int BH, int N, int d, int Bq, int P);
 hipError_t launch_probe(const void* q, const void* k, const void* v, void* o, int BH, int N, int d, int Bq,
-                        double scale, int P, double ridge, float* a_user, float* exact_user, void* ws,
+                        double scale, int P, double ridge, int rank, float* a_user, float* exact_user, void* ws,
                         hipStream_t stream);
 size_t kmeans_workspace_bytes(int BH, int N, int d, int C);
 hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, const float* init, float* cen,
@@ -365,14 +365,15 @@ size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int 
 }
 
 int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void* o, int dtype, int B, int H, int N,
-                              int d, int Bq, double scale, int probes, double ridge, float* a_out, float* exact_out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              int d, int Bq, double scale, int probes, double ridge, int rank, float* a_out,
+                              float* exact_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace) return fail(SA_ERR_INVALID_ARG, "probe_correct: null workspace");
   int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, 64, scale, o);
   if (rc) return rc;
   if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "probe_correct: only SA_BF16 tensors are supported");
   if (probes < 1 || probes > 1024) return fail(SA_ERR_INVALID_ARG, "probe_correct: probes=%d not in [1, 1024]", probes);
   if (!(ridge > 0.0) || !isfinite(ridge)) return fail(SA_ERR_INVALID_ARG, "probe_correct: ridge must be finite and > 0");
+  if (rank < 1) return fail(SA_ERR_INVALID_ARG, "probe_correct: rank=%d must be at least 1", rank);
   if ((reinterpret_cast<uintptr_t>(a_out) & 15u) || (reinterpret_cast<uintptr_t>(exact_out) & 15u))
     return fail(SA_ERR_INVALID_ARG, "probe_correct: a_out and exact_out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
@@ -384,7 +385,7 @@ int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void*
                 workspace_bytes, need);
   if ((long long)B * H * probes * cdiv(N, 64) > 0x7fffffffLL || (long long)B * H * cdiv(N, 256) > 0x7fffffffLL)
     return fail(SA_ERR_UNSUPPORTED, "probe_correct: too many workgroups");
-  return hip_status(sa::launch_probe(q, k, v, o, B * H, N, d, Bq, scale, probes, ridge, a_out, exact_out, workspace,
+  return hip_status(sa::launch_probe(q, k, v, o, B * H, N, d, Bq, scale, probes, ridge, rank, a_out, exact_out, workspace,
                                      static_cast<hipStream_t>(stream)),
                     "probe_correct launch");
 }

@@ -10,9 +10,12 @@
 //   3. X = [O_sparse, 1] and R = O_exact - O_sparse on the probe rows, G = X^T X and C = X^T R
 //      (float64);
 //   4. A = (G + mu I)^-1 C with mu = ridge * trace(G) / (d + 1), by Cholesky factorisation;
+//   4b. with a rank below d, A <- A V_r V_r^T: V_r the eigenvectors of R^T R for its rank largest
+//      eigenvalues (the principal directions of the probe residuals);
 //   5. O <- O + [O, 1] A on every row, in place.
 // Kernels: probe_partial (MFMA, the forward's tile layout), probe_combine, probe_gram (fp64 MFMA),
-// probe_chol and probe_subst (fp64) and probe_apply (bf16 MFMA, HBM-bound).
+// probe_chol and probe_subst (fp64), probe_subspace (fp32 Jacobi, with a rank below d) and
+// probe_apply (bf16 MFMA, HBM-bound).
 #include <algorithm>
 #include <type_traits>
 
@@ -310,9 +313,11 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(const float* __restr
 // the sequence zero) and R = O_exact - O_sparse; [G | C] = X^T Z is a (D + 1) x (2 D + 1) float64
 // product over the m = P BQ probe rows, on the matrix cores (v_mfma_f64_16x16x4f64: lane j holds
 // A[j % 16][j / 16] and B[j / 16][j % 16] of a 16x4 / 4x16 step; element i of the result is
-// C[4 i + j / 16][j % 16]). Grid (BH, ceil((D + 1) / 16)): a workgroup of 4 waves computes the
-// 16 rows i0 .. i0 + 15 of [G | C] (A = Z[:, i0 .. i0 + 15]^T), its waves splitting the 16-column
+// C[4 i + j / 16][j % 16]). Grid (BH, ceil(grows / 16)): a workgroup of 4 waves computes the
+// 16 rows i0 .. i0 + 15 of Z^T Z (A = Z[:, i0 .. i0 + 15]^T), its waves splitting the 16-column
 // tiles; Z is staged through LDS 16 probe rows at a time, the next stage prefetched in registers.
+// grows = D + 1 gives [G | C]; grows = 2 D + 1 gives all of Z^T Z, whose last D rows and columns
+// hold R^T R for the residual subspace.
 template <int D>
 struct GramCfg {
   static constexpr int n = D + 1, W = 2 * D + 1;
@@ -326,7 +331,8 @@ struct GramCfg {
 
 template <int D>
 __global__ __launch_bounds__(256) void probe_gram_kernel(const uint16_t* __restrict__ o, const float* __restrict__ exact,
-                                                         int N, int nqb, int BQ, int P, double* __restrict__ gram) {
+                                                         int N, int nqb, int BQ, int P, int grows,
+                                                         double* __restrict__ gram) {
   using G = GramCfg<D>;
   constexpr int n = G::n, W = G::W, NJ = G::NJ, ZW = G::ZW, ZS = G::ZS, CH = G::CH, EPT = G::EPT, TPW = G::TPW;
   __shared__ double z[CH * ZS];
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(256) void probe_gram_kernel(const uint16_t* __restr
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = i0 + 4 * i + jk;
-        if (row < n) gram[((size_t)bh * n + row) * W + col] = acc[t][i];
+        if (row < grows) gram[((size_t)bh * grows + row) * W + col] = acc[t][i];
       }
     }
   }
@@ -447,7 +453,7 @@ struct SolveCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(1024) void probe_chol_kernel(const double* __restrict__ gram, double ridge,
+__global__ __launch_bounds__(1024) void probe_chol_kernel(const double* __restrict__ gram, int grows, double ridge,
                                                           double* __restrict__ fac) {
   using S = SolveCfg<D>;
   constexpr int n = S::n, W = S::W, NT = S::NT, SS = S::SS, TRI = S::TRI, EPT = S::EPT;
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(1024) void probe_chol_kernel(const double* __restri
   double* invd = col + 2 * n;    // n: 1 / L[r][r]
   __shared__ double red[NT / 64];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const double* g = gram + (size_t)bh * n * W;
+  const double* g = gram + (size_t)bh * grows * W;
 
   for (int e = tid; e < n * SS; e += NT) Lf[e] = 0.0;
   double tr = 0.0;
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(1024) void probe_chol_kernel(const double* __restri
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void probe_subst_kernel(const double* __restrict__ gram,
+__global__ __launch_bounds__(256) void probe_subst_kernel(const double* __restrict__ gram, int grows,
                                                           const double* __restrict__ fac, float* __restrict__ a_out,
                                                           __bf16* __restrict__ at_out, float* __restrict__ bias_out) {
   using S = SolveCfg<D>;
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(256) void probe_subst_kernel(const double* __restri
   double* invd = Lf + n * SS;    // n
   double* ytmp = sm + S::FAC;    // 2 x RS x CW: one row block of the right-hand sides
   const int bh = blockIdx.x, c0 = blockIdx.y * CW, tid = threadIdx.x;
-  const double* g = gram + (size_t)bh * n * W;
+  const double* g = gram + (size_t)bh * grows * W;
   {
     const double2* src = reinterpret_cast<const double2*>(fac + (size_t)bh * S::FAC);
     double2* dst = reinterpret_cast<double2*>(sm);
@@ -687,6 +693,151 @@ __global__ __launch_bounds__(256) void probe_subst_kernel(const double* __restri
   }
 }
 
+// ---------------------------------------------------------------- 4b. residual subspace
+
+// The map confined to the output subspace observed in the probe residuals: A <- A V_r V_r^T with
+// V_r the eigenvectors of R^T R (the last D rows and columns of Z^T Z) for its `rank` largest
+// eigenvalues. One workgroup of 512 threads per head; R^T R and the eigenvector matrix sit in LDS
+// as fp32 (rows padded by one float). Cyclic Jacobi: each sweep runs D - 1 rounds of D / 2
+// disjoint pairs (the round-robin pairing: index 0 fixed, the others rotated by one per round);
+// a round computes every pair's rotation (c, s) annihilating S[p][q], then rotates rows p and q
+// of S for all pairs, then columns p and q of S and of V (S <- J^T S J, V <- V J). Sweeps stop when
+// the off-diagonal mass is below 1e-12 of the total, after at most kJacobiSweeps. Eigenvalue i
+// ranks by (descending S[i][i], index); the projector P = sum over the kept i of v_i v_i^T replaces
+// S, A (fp32, from the substitution) replaces V, and A P is written back as A, A^T (bf16) and the
+// bias row, the formats of the substitution kernel.
+constexpr int kJacobiSweeps = 20;
+template <int D>
+struct SubCfg {
+  static constexpr int NT = 512, P = D + 1;
+  static constexpr size_t LDS = (size_t)2 * D * P * 4 + (size_t)(D + 2 * (D / 2) + 32) * 4;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert((size_t)(D + 1) * D <= (size_t)D * P, "A must fit in the eigenvector space");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void probe_subspace_kernel(const double* __restrict__ gram, int rank,
+                                                             float* __restrict__ a_io, __bf16* __restrict__ at_out,
+                                                             float* __restrict__ bias_out) {
+  using C = SubCfg<D>;
+  constexpr int n = D + 1, W = 2 * D + 1, P = C::P, NT = C::NT, NP = D / 2;
+  extern __shared__ __attribute__((aligned(16))) float sub_sm[];
+  float* S = sub_sm;               // D x P
+  float* V = S + D * P;            // D x P
+  float* lam = V + D * P;          // D
+  float* rc = lam + D;             // NP rotation cosines
+  float* rsn = rc + NP;            // NP rotation sines
+  float* red = rsn + NP;           // 32 partial sums
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const double* g = gram + ((size_t)bh * W + n) * W + n;  // R^T R, row stride W
+  for (int e = tid; e < D * D; e += NT) {
+    const int i = e / D, j = e % D;
+    S[i * P + j] = (float)g[(size_t)i * W + j];
+    V[i * P + j] = i == j ? 1.f : 0.f;
+  }
+  __syncthreads();
+  // players of round k: 0, then 1 + (t - 1 + k) mod (D - 1) for t = 1 .. D - 1; pair i takes the
+  // players at positions i and D - 1 - i
+  auto player = [&](int t, int k) { return t == 0 ? 0 : 1 + (t - 1 + k) % (D - 1); };
+  for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+    for (int k = 0; k < D - 1; ++k) {
+      if (tid < NP) {
+        const int a = player(tid, k), b = player(D - 1 - tid, k);
+        const int p = min(a, b), q = max(a, b);
+        const float spp = S[p * P + p], sqq = S[q * P + q], spq = S[p * P + q];
+        float c = 1.f, sn = 0.f;
+        if (fabsf(spq) > 1e-30f && fabsf(spq) > 1e-9f * sqrtf(fabsf(spp * sqq))) {
+          const float tau = (sqq - spp) / (2.f * spq);
+          const float t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
+          c = 1.f / sqrtf(1.f + t * t);
+          sn = t * c;
+        }
+        rc[tid] = c;
+        rsn[tid] = sn;
+      }
+      __syncthreads();
+      for (int e = tid; e < NP * D; e += NT) {  // rows p, q of S
+        const int i = e / D, j = e % D;
+        const int a = player(i, k), b = player(D - 1 - i, k);
+        const int p = min(a, b), q = max(a, b);
+        const float c = rc[i], sn = rsn[i];
+        const float x = S[p * P + j], y = S[q * P + j];
+        S[p * P + j] = c * x - sn * y;
+        S[q * P + j] = sn * x + c * y;
+      }
+      __syncthreads();
+      for (int e = tid; e < NP * D; e += NT) {  // columns p, q of S and V
+        const int i = e % NP, j = e / NP;
+        const int a = player(i, k), b = player(D - 1 - i, k);
+        const int p = min(a, b), q = max(a, b);
+        const float c = rc[i], sn = rsn[i];
+        const float x = S[j * P + p], y = S[j * P + q];
+        S[j * P + p] = c * x - sn * y;
+        S[j * P + q] = sn * x + c * y;
+        const float u = V[j * P + p], w = V[j * P + q];
+        V[j * P + p] = c * u - sn * w;
+        V[j * P + q] = sn * u + c * w;
+      }
+      __syncthreads();
+    }
+    // off-diagonal mass against the total
+    float off = 0.f, tot = 0.f;
+    for (int e = tid; e < D * D; e += NT) {
+      const float x = S[(e / D) * P + e % D];
+      tot += x * x;
+      if (e / D != e % D) off += x * x;
+    }
+    for (int m = 32; m > 0; m >>= 1) {
+      off += __shfl_xor(off, m);
+      tot += __shfl_xor(tot, m);
+    }
+    if ((tid & 63) == 0) {
+      red[tid >> 6] = off;
+      red[16 + (tid >> 6)] = tot;
+    }
+    __syncthreads();
+    float o2 = 0.f, t2 = 0.f;
+    for (int w = 0; w < NT / 64; ++w) {
+      o2 += red[w];
+      t2 += red[16 + w];
+    }
+    __syncthreads();
+    if (o2 <= 1e-12f * t2) break;  // uniform: every thread read the same sums
+  }
+  if (tid < D) lam[tid] = S[tid * P + tid];
+  __syncthreads();
+  // kept eigenvectors: rank by (descending eigenvalue, index)
+  bool keep_i = false;
+  if (tid < D) {
+    int r = 0;
+    const float li = lam[tid];
+    for (int j = 0; j < D; ++j) r += (lam[j] > li || (lam[j] == li && j < tid)) ? 1 : 0;
+    keep_i = r < rank;
+  }
+  __syncthreads();
+  if (tid < D) lam[tid] = keep_i ? 1.f : 0.f;  // lam now flags the kept eigenvectors
+  __syncthreads();
+  for (int e = tid; e < D * D; e += NT) {  // projector into S
+    const int a = e / D, b = e % D;
+    float x = 0.f;
+    for (int i = 0; i < D; ++i) x = fmaf(V[a * P + i] * lam[i], V[b * P + i], x);
+    S[a * P + b] = x;
+  }
+  __syncthreads();
+  float* A = V;  // (D + 1) x D, row stride D
+  float* ah = a_io + (size_t)bh * n * D;
+  for (int e = tid; e < n * D; e += NT) A[e] = ah[e];
+  __syncthreads();
+  for (int e = tid; e < n * D; e += NT) {
+    const int row = e / D, col = e % D;
+    float x = 0.f;
+    for (int a = 0; a < D; ++a) x = fmaf(A[row * D + a], S[a * P + col], x);
+    ah[e] = x;
+    if (row < D) at_out[((size_t)bh * D + col) * D + row] = (__bf16)x;
+    else bias_out[(size_t)bh * D + col] = x;
+  }
+}
+
 // ---------------------------------------------------------------- 5. O <- O + O A[0:D] + A[D]
 
 // Grid BH x ceil(N / ROWS): each workgroup (4 waves) keeps A[0:D]^T (bf16) of its head in LDS and
@@ -794,7 +945,7 @@ ProbeWs probe_ws_layout(int BH, int N, int d, int Bq, int P) {
   w.exact = off;
   off += al256((size_t)BH * P * Bq * d * 4);
   w.gram = off;
-  off += al256((size_t)BH * (d + 1) * (2 * d + 1) * 8);
+  off += al256((size_t)BH * (2 * d + 1) * (2 * d + 1) * 8);  // Z^T Z (rows past d + 1 only with a rank)
   w.fac = off;
   off += al256((size_t)BH * (d == 128 ? SolveCfg<128>::FAC : SolveCfg<64>::FAC) * 8);
   w.amat = off;
@@ -812,7 +963,8 @@ size_t probe_workspace_bytes(int BH, int N, int d, int Bq, int P) { return probe
 
 template <int D, int BQ>
 static hipError_t launch_probe_t(const void* q, const void* k, const void* v, void* o, int BH, int N, float scale,
-                                 int P, double ridge, float* a_user, float* exact_user, void* ws, hipStream_t stream) {
+                                 int P, double ridge, int rank, float* a_user, float* exact_user, void* ws,
+                                 hipStream_t stream) {
   const int nqb = (N + BQ - 1) / BQ, nkb = (N + BK - 1) / BK;
   const int S = probe_splits(BH, P, nkb);
   const ProbeWs w = probe_ws_layout(BH, N, D, BQ, P);
@@ -836,21 +988,32 @@ static hipError_t launch_probe_t(const void* q, const void* k, const void* v, vo
   hipLaunchKernelGGL(probe_combine_kernel, dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, stream, part_o,
                      part_ml, rows, P, S, BQ, D, exact);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((probe_gram_kernel<D>), dim3((unsigned)BH, (unsigned)((D + 1 + 15) / 16)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(o), exact, N, nqb, BQ, P, gram);
+  const bool project = rank < D;
+  const int grows = project ? 2 * D + 1 : D + 1;
+  hipLaunchKernelGGL((probe_gram_kernel<D>), dim3((unsigned)BH, (unsigned)((grows + 15) / 16)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(o), exact, N, nqb, BQ, P, grows, gram);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   using SC = SolveCfg<D>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_chol_kernel<D>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)SC::CHOL_LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((probe_chol_kernel<D>), dim3((unsigned)BH), dim3(SC::NT), SC::CHOL_LDS, stream, gram, ridge, fac);
+  hipLaunchKernelGGL((probe_chol_kernel<D>), dim3((unsigned)BH), dim3(SC::NT), SC::CHOL_LDS, stream, gram, grows, ridge,
+                     fac);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_subst_kernel<D>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)SC::SUBST_LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((probe_subst_kernel<D>), dim3((unsigned)BH, (unsigned)(D / SC::CW)), dim3(SC::ST), SC::SUBST_LDS,
-                     stream, gram, fac, amat, at, bias);
+                     stream, gram, grows, fac, amat, at, bias);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (project) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&probe_subspace_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)SubCfg<D>::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((probe_subspace_kernel<D>), dim3((unsigned)BH), dim3(SubCfg<D>::NT), SubCfg<D>::LDS, stream,
+                       gram, rank, amat, at, bias);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int tph = (N + kApplyRows - 1) / kApplyRows;
   hipLaunchKernelGGL((probe_apply_kernel<D>), dim3((unsigned)(BH * tph)), dim3(256), 0, stream,
                      static_cast<uint16_t*>(o), at, bias, N, tph, kApplyRows);
@@ -858,13 +1021,17 @@ static hipError_t launch_probe_t(const void* q, const void* k, const void* v, vo
 }
 
 hipError_t launch_probe(const void* q, const void* k, const void* v, void* o, int BH, int N, int d, int Bq,
-                        double scale, int P, double ridge, float* a_user, float* exact_user, void* ws,
+                        double scale, int P, double ridge, int rank, float* a_user, float* exact_user, void* ws,
                         hipStream_t stream) {
   const float sc = (float)scale;
-  if (d == 128 && Bq == 128) return launch_probe_t<128, 128>(q, k, v, o, BH, N, sc, P, ridge, a_user, exact_user, ws, stream);
-  if (d == 128 && Bq == 64) return launch_probe_t<128, 64>(q, k, v, o, BH, N, sc, P, ridge, a_user, exact_user, ws, stream);
-  if (d == 64 && Bq == 128) return launch_probe_t<64, 128>(q, k, v, o, BH, N, sc, P, ridge, a_user, exact_user, ws, stream);
-  if (d == 64 && Bq == 64) return launch_probe_t<64, 64>(q, k, v, o, BH, N, sc, P, ridge, a_user, exact_user, ws, stream);
+#define SA_PROBE_CASE(D_, BQ_)                                                                                   \
+  if (d == D_ && Bq == BQ_)                                                                                      \
+    return launch_probe_t<D_, BQ_>(q, k, v, o, BH, N, sc, P, ridge, rank, a_user, exact_user, ws, stream);
+  SA_PROBE_CASE(128, 128)
+  SA_PROBE_CASE(128, 64)
+  SA_PROBE_CASE(64, 128)
+  SA_PROBE_CASE(64, 64)
+#undef SA_PROBE_CASE
   return hipErrorInvalidValue;
 }
 

@@ -285,12 +285,16 @@ size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int 
  *   fit       X = [O, 1] and R = O_exact - O on the probe rows inside the sequence (duplicated
  *             probes count once per occurrence); A = (X^T X + mu I)^-1 X^T R in float64 by
  *             Cholesky, mu = ridge * trace(X^T X) / (d + 1);
+ *   subspace  with rank < d, A <- A V_r V_r^T, V_r the eigenvectors of R^T R for its `rank` largest
+ *             eigenvalues (the principal directions of the probe residuals; cyclic Jacobi in
+ *             fp32 on R^T R formed in float64), so that every correction row lies in their span;
  *   apply     O <- O + O A[0:d] + A[d] on every row (bf16 MFMA with A rounded to bf16, fp32
  *             accumulation and add, result rounded to bf16).
  *   q, k, v     device, [B, H, N, d] SA_BF16 (`dtype` must be SA_BF16).
  *   o           device in/out, [B, H, N, d] bf16: the sparse output (e.g. of sparse_attn_fwd), replaced
  *               by the corrected output.
- *   probes      1 .. 1024; ridge > 0 (then X^T X + mu I is positive definite).
+ *   probes      1 .. 1024; ridge > 0 (then X^T X + mu I is positive definite); rank >= 1 (rank >= d:
+ *               no projection).
  *   a_out       device out or NULL, [B, H, d + 1, d] float32: A.
  *   exact_out   device out or NULL, [B, H, probes * Bq, d] float32: the exact probe rows in probe
  *               order (rows past N, possible only when the sequence has no full block, are
@@ -300,8 +304,8 @@ size_t sparse_attn_probe_workspace_size(int B, int H, int N, int d, int Bq, int 
  * d in {64, 128}, Bq in {64, 128}; key blocks of 64. Deterministic (no atomics).
  */
 int sparse_attn_probe_correct(const void* q, const void* k, const void* v, void* o, int dtype, int B, int H, int N,
-                              int d, int Bq, double scale, int probes, double ridge, float* a_out, float* exact_out,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              int d, int Bq, double scale, int probes, double ridge, int rank, float* a_out,
+                              float* exact_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Semantic-aware permutation ([SVG2] "2. 手法" A, B, C): tokens are grouped by k-means on Q and on

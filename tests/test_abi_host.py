@@ -273,7 +273,7 @@ def test_bwd_workspace_size():
 def _probe(**kw):
     ws = _lib.lib().sparse_attn_probe_workspace_size(1, 2, 1024, 64, 64, 2)
     a = dict(q=P, k=P, v=P, o=P, dtype=0, B=1, H=2, N=1024, d=64, Bq=64, scale=0.125, probes=2, ridge=1e-3,
-             a_out=None, exact_out=None, ws=P, ws_bytes=ws, stream=None)
+             rank=8, a_out=None, exact_out=None, ws=P, ws_bytes=ws, stream=None)
     a.update(kw)
     return _lib.lib().sparse_attn_probe_correct(*a.values())
 
@@ -282,7 +282,8 @@ def _probe(**kw):
     (dict(o=None), -1), (dict(q=None), -1), (dict(ws=None), -1), (dict(ws_bytes=64), -1), (dict(ws=P + 16), -1),
     (dict(o=P_ODD), -1), (dict(a_out=P_ODD), -1), (dict(exact_out=P_ODD), -1), (dict(probes=0), -1),
     (dict(probes=1025), -1), (dict(ridge=0.0), -1), (dict(ridge=float("nan")), -1), (dict(scale=-1.0), -1),
-    (dict(dtype=1), -2), (dict(d=96), -2), (dict(Bq=32), -2), (dict(N=0), -1),
+    (dict(dtype=1), -2), (dict(d=96), -2), (dict(Bq=32), -2), (dict(N=0), -1), (dict(rank=0), -1),
+    (dict(rank=-3), -1),
 ])
 def test_probe_correct_rejects(kw, code):
     assert _probe(**kw) == code
@@ -291,8 +292,9 @@ def test_probe_correct_rejects(kw, code):
 def test_probe_workspace_size():
     """Partial outputs of S key-block ranges (S minimises rounds of 512 workgroups times key
     blocks per range, at most 24 ranges, at least 4 key blocks per range), the exact probe rows,
-    [G | C] in float64, the factor (rows padded to blocks of 8 plus the n reciprocals of its
-    diagonal, an even count of float64), A, A^T in bf16 and the bias row."""
+    Z^T Z = [X | R]^T [X | R] in float64 (its last d rows only with a rank below d), the factor
+    (rows padded to blocks of 8 plus the n reciprocals of its diagonal, an even count of float64),
+    A, A^T in bf16 and the bias row."""
     lib = _lib.lib()
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     bh, n, d, bq, probes = 2, 1000, 128, 128, 3
@@ -304,7 +306,8 @@ def test_probe_workspace_size():
     m = d + 1
     fac = (m * (-(-m // 8) * 8) + m + 1) // 2 * 2
     want = al(units * bq * d * 4) + al(units * bq * 8) + al(bh * probes * bq * d * 4) + \
-        al(bh * m * (2 * d + 1) * 8) + al(bh * fac * 8) + al(bh * m * d * 4) + al(bh * d * d * 2) + al(bh * d * 4)
+        al(bh * (2 * d + 1) * (2 * d + 1) * 8) + al(bh * fac * 8) + al(bh * m * d * 4) + al(bh * d * d * 2) + \
+        al(bh * d * 4)
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, probes) == want
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, 96, bq, probes) == 0
     assert lib.sparse_attn_probe_workspace_size(1, 2, n, d, bq, 0) == 0
