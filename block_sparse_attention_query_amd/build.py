@@ -15,7 +15,14 @@ LIB = os.path.join(HERE, "libsparse_attn.so")
 SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "patterns.hip", "probe.hip", "cluster.hip"]
 # Per-source extra flags. The attention kernels assume finite-or-infinite inputs (NaN inputs give
 # unspecified outputs), which lets fmaxf on MFMA results skip the NaN-quieting canonicalize.
-EXTRA = {"attn_fwd.hip": ["-fno-honor-nans"], "attn_bwd.hip": ["-fno-honor-nans"], "probe.hip": ["-fno-honor-nans"], "cluster.hip": ["-fno-honor-nans"]}
+# Matrix-core sources also take the VGPR form of every MFMA (results and accumulators in
+# architectural VGPRs): by default the compiler places MFMA results in AGPRs, and kernels whose
+# products feed vector arithmetic (the softmax of S, dS from dP) then spend one v_accvgpr_read per
+# element, plus accumulator moves whenever the AGPR tuples fragment (160 of the 490 vector
+# instructions of a dK/dV step on D = 128).
+MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+EXTRA = {"attn_fwd.hip": ["-fno-honor-nans", *MFMA_VGPR], "attn_bwd.hip": ["-fno-honor-nans", *MFMA_VGPR],
+         "probe.hip": ["-fno-honor-nans", *MFMA_VGPR], "cluster.hip": ["-fno-honor-nans", *MFMA_VGPR]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.

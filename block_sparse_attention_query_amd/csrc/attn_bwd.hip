@@ -41,19 +41,28 @@ __global__ __launch_bounds__(256) void mask_transpose_kernel(const uint8_t* __re
 // Two ds_read_b64_tr_b16 per lane: within each 16-lane group, lane s addresses row
 // row0 + 8 u + 4 (group / 2) + s / 4 at columns col0 + 16 (group % 2) + 4 (s % 4) .. + 3, so lane i
 // of the group receives column col0 + 16 (group % 2) + i of four consecutive rows.
+// The swizzle of a row depends only on its low four bits, so for row0 a multiple of 16 the two
+// read addresses are tile + off[u] + row0 ROWB with lane offsets off[u] that depend on col0 alone:
+// tr_offsets computes them once, and tr_read adds row0 ROWB as an immediate.
 template <int ROWB, int SWZD>
-__device__ __forceinline__ bf16x8 tr_operand(const lchar* tile, int row0, int col0, int lane) {
+__device__ __forceinline__ void tr_offsets(int col0, int lane, int* off) {
   const int i16 = lane & 15, grp = lane >> 4;
   const int half = grp >> 1, gsub = grp & 1;
-  v4i16 part[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int row = row0 + 8 * u + 4 * half + (i16 >> 2);
+    const int row = 8 * u + 4 * half + (i16 >> 2);
     const int chunk = ((col0 + 16 * gsub) >> 3) + ((i16 & 3) >> 1);
-    const int off = row * ROWB + ((chunk ^ kv_swz<SWZD>(row)) << 4) + (i16 & 1) * 8;
-    part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lchar*>(tile) + off));
+    off[u] = row * ROWB + ((chunk ^ kv_swz<SWZD>(row)) << 4) + (i16 & 1) * 8;
   }
+}
+
+template <int ROWB>
+__device__ __forceinline__ bf16x8 tr_read(const lchar* tile, const int* off, int row0) {
+  v4i16 part[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    part[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(const_cast<lchar*>(tile) + off[u] + row0 * ROWB));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -61,8 +70,9 @@ __device__ __forceinline__ bf16x8 tr_operand(const lchar* tile, int row0, int co
 
 // One workgroup per (b, h, query block), BQ / 32 waves of 32 queries, walking the kept list:
 //   S^T = K Q^T, dP^T = V dO^T (A operands: 16-byte row reads of the K and V tiles),
-//   dS^T = P^T * (dP^T - D) * scale in registers (the B operand layout of the forward's P^T),
-//   dQ^T += K^T dS^T (K^T by transpose reads of the K tile).
+//   dS^T = P^T * (dP^T - D) in registers (the B operand layout of the forward's P^T),
+//   dQ^T += K^T dS^T (K^T by transpose reads of the K tile); the scale multiplies dQ once, in the
+//   epilogue.
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, const void* __restrict__ dout,
@@ -138,21 +148,18 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) koff[s] = ln * C::ROWB + (((2 * s + hf) ^ sw) << 4);
   }
+  int toff[D / 32][2];  // transpose-read offsets of K^T, channel tile r
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r) tr_offsets<C::ROWB, D>(32 * r, lane, toff[r]);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int r = 0; r < D / 32; ++r)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
 
-  for (int t = 0; t < cnt; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block t is resident; every wave is done with the other buffer
-    if (t + 1 < cnt) {
-      lchar* nb = (t & 1) ? buf0 : buf1;
-      dma_tile<D, BQ>(kbase, blk(t + 1), N, wave, lane, doff, nb);
-      dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, nb + C::TILE);
-    }
-    const lchar* kt = (t & 1) ? buf1 : buf0;
+  // Block t of the list sits in buffer t & 1. The walk is unrolled by two so that each copy of the
+  // step reads a fixed buffer and its base folds into the LDS reads' immediate offsets.
+  auto step = [&](int t, const lchar* kt) {
     const lchar* vt = kt + C::TILE;
     const int kb = blk(t);
     f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
@@ -171,8 +178,12 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (key >= N) s0[i] = -INFINITY;
-        if (key + 32 >= N) s1[i] = -INFINITY;
+        float a = key >= N ? -INFINITY : s0[i], b = key + 32 >= N ? -INFINITY : s1[i];
+        // the empty asm cannot be speculated, which keeps this a branch: as selects hoisted out
+        // of it the mask would cost every block
+        asm volatile("" : "+v"(a), "+v"(b));
+        s0[i] = a;
+        s1[i] = b;
       }
     }
     // dS^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t
@@ -186,8 +197,8 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 8 * u + 2 * e + h;
-          x[h] = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse2)) * (p0[i] - dlt) * scale;
-          x[2 + h] = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse2)) * (p1[i] - dlt) * scale;
+          x[h] = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse2)) * (p0[i] - dlt);
+          x[2 + h] = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse2)) * (p1[i] - dlt);
         }
         w0[e] = pack_bf16(x[0], x[1]);
         w1[e] = pack_bf16(x[2], x[3]);
@@ -200,8 +211,25 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int r = 0; r < D / 32; ++r)
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<C::ROWB, D>(kt, 16 * c, 32 * r, lane), db[c],
-                                                          acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<C::ROWB>(kt, toff[r], 16 * c), db[c], acc[r], 0, 0, 0);
+  };
+  for (int t = 0; t < cnt; t += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block t is resident in buffer 0; every wave is done with buffer 1
+    if (t + 1 < cnt) {
+      dma_tile<D, BQ>(kbase, blk(t + 1), N, wave, lane, doff, buf1);
+      dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, buf1 + C::TILE);
+    }
+    step(t, buf0);
+    if (t + 1 < cnt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // block t + 1 is resident in buffer 1; every wave is done with buffer 0
+      if (t + 2 < cnt) {
+        dma_tile<D, BQ>(kbase, blk(t + 2), N, wave, lane, doff, buf0);
+        dma_tile<D, BQ>(vbase, blk(t + 2), N, wave, lane, doff, buf0 + C::TILE);
+      }
+      step(t + 1, buf1);
+    }
   }
   __syncthreads();
 
@@ -212,7 +240,8 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int ch = 32 * r + 8 * a + 4 * hf;
-      const u32x2 w = {pack_bf16(acc[r][4 * a], acc[r][4 * a + 1]), pack_bf16(acc[r][4 * a + 2], acc[r][4 * a + 3])};
+      const u32x2 w = {pack_bf16(acc[r][4 * a] * scale, acc[r][4 * a + 1] * scale),
+                       pack_bf16(acc[r][4 * a + 2] * scale, acc[r][4 * a + 3] * scale)};
       *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(ol + ln * C::OROW + ch * 2) = w;
     }
   __syncthreads();
@@ -371,6 +400,9 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     for (int s = 0; s < D / 16; ++s) roff[s] = ln * C::ROWB + (((2 * s + hf) ^ sw) << 4);
   }
 
+  int toff[D / 32][2];  // transpose-read offsets of dO and Q, channel tile c
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) tr_offsets<C::ROWB, D>(32 * c, lane, toff[c]);
   f32x16 acc_k[D / 32], acc_v[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
@@ -380,16 +412,17 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       acc_v[c][i] = 0.f;
     }
 
-  for (int t = 0; t < T; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // step t is resident; both waves are done with the buffer of step t - 1
-    if (t + 1 < T) SA_KV_ISSUE(t + 1)
-    const lchar* qt = base + (t & 1) * C::BUF;
+  // Step t sits in buffer t & 1. The walk is unrolled by two so that each copy of the step reads
+  // a fixed buffer and its base folds into the LDS reads' immediate offsets.
+  auto step = [&](const lchar* qt) {
     const lchar* gt = qt + C::OFF_G;
 
     // S = Q K^T and dP = dO V^T for queries 32 h .. 32 h + 31 of the step: element i of lane
-    // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4. The A operands of
-    // channel slice s + 1 are read while the products of slice s run.
+    // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4.
+    // The step runs in four phases so that the vector work lies under matrix products of the same
+    // wave (one wave per SIMD): A. S, dP of half 0; B. S, dP of half 1, with P and dS of half 0
+    // computed between the products; C. dV, dK of half 0, with P and dS of half 1 between them;
+    // D. dV, dK of half 1. Operands are read one product step ahead throughout.
     f32x16 sc[2], dp[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -398,89 +431,97 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
         sc[h][i] = 0.f;
         dp[h][i] = 0.f;
       }
-    bf16x8 cur[4], nxt[4];
+    // P = exp(s - LSE) and dS = P (dP - D) (the scale multiplies dK in the epilogue) of queries 32 h + 16 u + 8 g + 4 hf .. + 3,
+    // packed to bf16 as words 2 g, 2 g + 1 of the A operands of run u of half h (elements
+    // 8 u + 4 g .. + 3)
+    uint32_t wp[2][2][4], ws[2][2][4];
+    auto ps_quad = [&](int h, int u, int g) {
+      const int qi = 32 * h + 16 * u + 8 * g + 4 * hf;
+      const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_L + qi * 4);
+      const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_D + qi * 4);
+      float pv[4], sv[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      cur[2 * h] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[0] + 32 * h * C::ROWB);
-      cur[2 * h + 1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[0] + 32 * h * C::ROWB);
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * u + 4 * g + e;
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[h][i], c_log2, -lv[e]));
+        sv[e] = pv[e] * (dp[h][i] - dv4[e]);
+      }
+      wp[h][u][2 * g] = pack_bf16(pv[0], pv[1]);
+      wp[h][u][2 * g + 1] = pack_bf16(pv[2], pv[3]);
+      ws[h][u][2 * g] = pack_bf16(sv[0], sv[1]);
+      ws[h][u][2 * g + 1] = pack_bf16(sv[2], sv[3]);
+      // empty asms keep this work where the schedule puts it (IR passes would sink it to its use)
+      asm volatile("" : "+v"(wp[h][u][2 * g]), "+v"(wp[h][u][2 * g + 1]), "+v"(ws[h][u][2 * g]),
+                   "+v"(ws[h][u][2 * g + 1]));
+    };
+    // phases A and B: step n = 8 h + s of the S / dP products
+    constexpr int SS = D / 16;
+    bf16x8 cur[2], nxt[2];
+    cur[0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[0]);
+    cur[1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[0]);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      if (s + 1 < D / 16) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          nxt[2 * h] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s + 1] + 32 * h * C::ROWB);
-          nxt[2 * h + 1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s + 1] + 32 * h * C::ROWB);
-        }
+    for (int n = 0; n < 2 * SS; ++n) {
+      const int h = n / SS, s = n % SS;
+      if (n + 1 < 2 * SS) {
+        const int h1 = (n + 1) / SS, s1 = (n + 1) % SS;
+        nxt[0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s1] + 32 * h1 * C::ROWB);
+        nxt[1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s1] + 32 * h1 * C::ROWB);
+      }
+      sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[0], kf[s], sc[h], 0, 0, 0);
+      dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[1], vf[s], dp[h], 0, 0, 0);
+      // half 0's P and dS under half 1's products (four quads over its SS steps)
+      if (h == 1 && (s % (SS / 4)) == (SS / 4) - 1) {
+        const int qd = s / (SS / 4);
+        ps_quad(0, qd >> 1, qd & 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[2 * h], kf[s], sc[h], 0, 0, 0);
-        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[2 * h + 1], vf[s], dp[h], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
     }
 
-    // the first transposed operands of the dV / dK products, read ahead of the softmax work
-    bf16x8 cg = tr_operand<C::ROWB, D>(gt, 0, 0, lane), cq = tr_operand<C::ROWB, D>(qt, 0, 0, lane);
-
-    // P = exp(s - LSE) and dS = P (dP - D) scale, packed to bf16 as A operands: run u of half h
-    // takes elements 8 u .. 8 u + 7, i.e. queries 32 h + 16 u + 8 (e / 4) + 4 hf + e % 4
-    bf16x8 pa[2][2], sa[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint32_t wp[4], ws[4];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int qi = 32 * h + 16 * u + 8 * g + 4 * hf;  // four consecutive queries
-          const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_L + qi * 4);
-          const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(qt + C::OFF_D + qi * 4);
-          float pv[4], sv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * u + 4 * g + e;
-            pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[h][i], c_log2, -lv[e]));
-            sv[e] = pv[e] * (dp[h][i] - dv4[e]) * scale;
-          }
-          wp[2 * g] = pack_bf16(pv[0], pv[1]);
-          wp[2 * g + 1] = pack_bf16(pv[2], pv[3]);
-          ws[2 * g] = pack_bf16(sv[0], sv[1]);
-          ws[2 * g + 1] = pack_bf16(sv[2], sv[3]);
-        }
-        pa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-        sa[h][u] = __builtin_bit_cast(bf16x8, make_uint4(ws[0], ws[1], ws[2], ws[3]));
-      }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // dV += P^T dO and dK += dS^T Q over the step's 64 queries, item j = (h, u, channel tile c);
-    // the operands of item j + 1 are read while the products of item j run
+    // phases C and D: dV += P^T dO and dK += dS^T Q, item j = (h, u, channel tile c); the
+    // transposed operands of item j + 1 are read while the products of item j run
     constexpr int NC = D / 32;
+    bf16x8 cg = tr_read<C::ROWB>(gt, toff[0], 0), cq = tr_read<C::ROWB>(qt, toff[0], 0);
 #pragma unroll
     for (int j = 0; j < 4 * NC; ++j) {
       const int h = j / (2 * NC), u = (j / NC) & 1, c = j % NC;
       bf16x8 ng = cg, nq = cq;
       if (j + 1 < 4 * NC) {
         const int h1 = (j + 1) / (2 * NC), u1 = ((j + 1) / NC) & 1, c1 = (j + 1) % NC;
-        ng = tr_operand<C::ROWB, D>(gt, 32 * h1 + 16 * u1, 32 * c1, lane);
-        nq = tr_operand<C::ROWB, D>(qt, 32 * h1 + 16 * u1, 32 * c1, lane);
+        ng = tr_read<C::ROWB>(gt, toff[c1], 32 * h1 + 16 * u1);
+        nq = tr_read<C::ROWB>(qt, toff[c1], 32 * h1 + 16 * u1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][u], cg, acc_v[c], 0, 0, 0);
-      acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][u], cq, acc_k[c], 0, 0, 0);
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(wp[h][u][0], wp[h][u][1], wp[h][u][2], wp[h][u][3]));
+      const bf16x8 sa = __builtin_bit_cast(bf16x8, make_uint4(ws[h][u][0], ws[h][u][1], ws[h][u][2], ws[h][u][3]));
+      acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, cg, acc_v[c], 0, 0, 0);
+      acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, cq, acc_k[c], 0, 0, 0);
+      // half 1's P and dS under half 0's products (four quads over the 2 NC items of half 0)
+      if (h == 0 && (j % (2 * NC / 4)) == (2 * NC / 4) - 1) {
+        const int qd = j / (2 * NC / 4);
+        ps_quad(1, qd >> 1, qd & 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       cg = ng;
       cq = nq;
+    }
+  };
+  for (int t = 0; t < T; t += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // step t is resident in buffer 0; both waves are done with buffer 1
+    if (t + 1 < T) SA_KV_ISSUE(t + 1)
+    step(base);
+    if (t + 1 < T) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // step t + 1 is resident in buffer 1; both waves are done with buffer 0
+      if (t + 2 < T) SA_KV_ISSUE(t + 2)
+      step(base + C::BUF);
     }
   }
 #undef SA_KV_ISSUE
   __syncthreads();  // every wave is done with the last step's buffer
 
-  // epilogue: dK then dV, staged through LDS as [key][channel] rows. Element i of tile c: channel
+  // epilogue: dK (times the scale) then dV, staged through LDS as [key][channel] rows. Element i of tile c: channel
   // 32 c + ln, key 32 w + 8 (i / 4) + 4 hf + i % 4
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
@@ -490,7 +531,7 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       for (int i = 0; i < 16; ++i) {
         const int kr = 32 * wave + 8 * (i >> 2) + 4 * hf + (i & 3);
         *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base + kr * C::OROW + (32 * c + ln) * 2) =
-            (__bf16)acc[i];
+            (__bf16)(which == 0 ? acc[i] * scale : acc[i]);
       }
     }
     __syncthreads();
