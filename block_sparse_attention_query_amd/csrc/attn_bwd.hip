@@ -105,8 +105,8 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
   uint32_t doff[C::PER_WAVE];
   dma_offsets<D, BQ>(wave, lane, doff);
   if (cnt > 0) {
-    dma_tile<D, BQ>(kbase, blk(0), N, wave, lane, doff, buf0);
-    dma_tile<D, BQ>(vbase, blk(0), N, wave, lane, doff, buf0 + C::TILE);
+    dma_tile_rsrc<D, BQ>(kbase, blk(0), N, wave, doff, buf0);
+    dma_tile_rsrc<D, BQ>(vbase, blk(0), N, wave, doff, buf0 + C::TILE);
   }
 
   const int qrow = qb * BQ + wave * 32 + ln;
@@ -217,16 +217,16 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block t is resident in buffer 0; every wave is done with buffer 1
     if (t + 1 < cnt) {
-      dma_tile<D, BQ>(kbase, blk(t + 1), N, wave, lane, doff, buf1);
-      dma_tile<D, BQ>(vbase, blk(t + 1), N, wave, lane, doff, buf1 + C::TILE);
+      dma_tile_rsrc<D, BQ>(kbase, blk(t + 1), N, wave, doff, buf1);
+      dma_tile_rsrc<D, BQ>(vbase, blk(t + 1), N, wave, doff, buf1 + C::TILE);
     }
     step(t, buf0);
     if (t + 1 < cnt) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // block t + 1 is resident in buffer 1; every wave is done with buffer 0
       if (t + 2 < cnt) {
-        dma_tile<D, BQ>(kbase, blk(t + 2), N, wave, lane, doff, buf0);
-        dma_tile<D, BQ>(vbase, blk(t + 2), N, wave, lane, doff, buf0 + C::TILE);
+        dma_tile_rsrc<D, BQ>(kbase, blk(t + 2), N, wave, doff, buf0);
+        dma_tile_rsrc<D, BQ>(vbase, blk(t + 2), N, wave, doff, buf0 + C::TILE);
       }
       step(t + 1, buf1);
     }
