@@ -271,17 +271,15 @@ struct KVCfg {
   static constexpr int OFF_L = 2 * TILE;     // 64 floats: LSE * log2(e) (+inf on padded rows)
   static constexpr int OFF_D = 2 * TILE + 256;  // 64 floats: D (0 on padded rows)
   static constexpr int BUF = 2 * TILE + 512;
-  static constexpr int LDS = 2 * BUF;
   static constexpr int OROW = D * 2 + 16;    // bytes per staged output row
-  static_assert(64 * OROW <= LDS, "output staging must fit");
+  static_assert(64 * OROW <= BUF, "output staging must fit in one buffer");
 };
 
 // Copies of the 64-row tile sb (token rows 64 sb .. + 63) of a [N][D] bf16 tensor into a
 // swizzled LDS tile by the two waves: instruction u of wave w fills the 1 KiB stretch
 // m = w PW + u; lane i fills its bytes 16 i .. + 15, i.e. row (1024 m + 16 i) / ROWB and swizzled
 // chunk slot ((1024 m + 16 i) % ROWB) / 16, which holds logical chunk slot ^ kv_swz(row).
-// kv_dma_offsets gives each lane's byte offsets inside a tile; rows past N (only in the last
-// tile) are clamped to N - 1.
+// kv_dma_offsets gives each lane's byte offsets inside a tile.
 template <int D>
 struct KVDma {
   static constexpr int ROWB = 2 * D;
@@ -299,31 +297,33 @@ __device__ __forceinline__ void kv_dma_offsets(int wave, int lane, uint32_t* off
   }
 }
 
+// The copies of one step, as 2 PW + 1 single instructions per wave that the walk spreads between
+// matrix products: part u < PW fills the wave's stretch u of the Q tile, PW <= u < 2 PW stretch
+// u - PW of the dO tile, part 2 PW the step's 64 LSE (wave 0) or D (wave 1) values. The tiles go
+// through buffer descriptors covering query rows 64 sb .. N - 1, so rows past N read as zeros;
+// such padded queries have LSE +inf and D 0, which makes their P and dS zero.
+struct KVStep {
+  __amdgpu_buffer_rsrc_t rq, rg;
+  const float* ld;
+  lchar* dst;
+};
+
 template <int D>
-__device__ __forceinline__ void kv_dma(const char* __restrict__ base, int sb, int N, int wave, int lane,
-                                       const uint32_t* off, lchar* dst) {
-  constexpr int ROWB = KVDma<D>::ROWB, PW = KVDma<D>::PW;
-  const char* blk = base + (size_t)sb * 64 * ROWB;
-  // The empty asm marks each 32-bit offset as redefined at its use, so that the compiler cannot
-  // hoist 64-bit zero-extended copies of the offsets out of the walk; the copy then takes the
-  // uniform base in SGPRs and the 32-bit offset in one VGPR.
-  if (sb * 64 + 64 <= N) {
-#pragma unroll
-    for (int u = 0; u < PW; ++u) {
-      uint32_t o = off[u];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * PW + u) * 1024, 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < PW; ++u) {
-      const int row = ((wave * PW + u) * 1024 + lane * 16) / ROWB;
-      const int over = sb * 64 + row - (N - 1);
-      uint32_t o = over > 0 ? off[u] - (uint32_t)(over * ROWB) : off[u];
-      asm volatile("" : "+v"(o));
-      __builtin_amdgcn_global_load_lds(blk + o, dst + (wave * PW + u) * 1024, 16, 0, 0);
-    }
-  }
+__device__ __forceinline__ KVStep kv_step(const char* qbase, const char* gbase, const float* ldbase, int sb, int N,
+                                          lchar* dst) {
+  return {tile_rsrc(qbase, sb, N, KVDma<D>::ROWB), tile_rsrc(gbase, sb, N, KVDma<D>::ROWB), ldbase + sb * 64, dst};
+}
+
+// (a plain function: the host pass rejects templates whose bodies hold these copy builtins)
+__device__ __forceinline__ void kv_part(const KVStep& c, int wave, int lane, const uint32_t* off, int part, int pw,
+                                        int off_g, int off_l) {
+  if (part < pw)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rq, c.dst + (wave * pw + part) * 1024, 16, off[part], 0, 0, 0);
+  else if (part < 2 * pw)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rg, c.dst + off_g + (wave * pw + part - pw) * 1024, 16, off[part - pw],
+                                             0, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(c.ld + lane, c.dst + off_l + wave * 256, 4, 0, 0);
 }
 
 // One workgroup per (b, h, key block j), walking the 64-query steps of the query blocks that keep
@@ -342,8 +342,12 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     void* __restrict__ dv) {
   using C = KVCfg<D>;
   constexpr int SPB = BQ / 64;  // 64-query steps per query block
-  extern __shared__ __attribute__((aligned(1024))) char lds_[];
-  lchar* const base = (lchar*)lds_;
+  // the two buffers are separate arrays, so that the compiler can tell the reads of one from the
+  // copies into the other and does not wait for those copies before the transpose reads
+  __shared__ __attribute__((aligned(1024))) char buf0_[C::BUF];
+  __shared__ __attribute__((aligned(1024))) char buf1_[C::BUF];
+  lchar* const base0 = (lchar*)buf0_;
+  lchar* const base1 = (lchar*)buf1_;
 
   const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nkb;
@@ -367,18 +371,15 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
   const float* dlbase = deltap + (size_t)bh * NP;
   uint32_t doff[KVDma<D>::PW];
   kv_dma_offsets<D>(wave, lane, doff);
-  // copies of step t into buffer t & 1: both tiles, then wave 0 the LSE and wave 1 the D values
-#define SA_KV_ISSUE(T_)                                                                                  \
-  {                                                                                                      \
-    const int t_ = (T_);                                                                                 \
-    const int sb_ = min(max(list[t_ / SPB], 0), nqb - 1) * SPB + t_ % SPB;                               \
-    lchar* b_ = base + (t_ & 1) * C::BUF;                                                                \
-    kv_dma<D>(qbase, sb_, N, wave, lane, doff, b_);                                                      \
-    kv_dma<D>(gbase, sb_, N, wave, lane, doff, b_ + C::OFF_G);                                           \
-    __builtin_amdgcn_global_load_lds((wave == 0 ? l2base : dlbase) + sb_ * 64 + lane, b_ + C::OFF_L + wave * 256, \
-                                     4, 0, 0);                                                           \
+  const float* ldbase = wave == 0 ? l2base : dlbase;
+  constexpr int NPART = 2 * KVDma<D>::PW + 1;  // copy instructions per wave and step
+  // query sub-block of step t (list entries clamped to [0, nQB))
+  auto sbof = [&](int t) { return min(max(list[t / SPB], 0), nqb - 1) * SPB + t % SPB; };
+  if (T > 0) {
+    const KVStep c0 = kv_step<D>(qbase, gbase, ldbase, sbof(0), N, base0);
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) kv_part(c0, wave, lane, doff, part, KVDma<D>::PW, C::OFF_G, C::OFF_L);
   }
-  if (T > 0) SA_KV_ISSUE(0)
 
   // K and V rows of key 32 w + ln, channels 16 s + 8 hf .. + 7: the B operands (keys past N are 0)
   const int key = kb * BK + wave * 32 + ln;
@@ -413,9 +414,12 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     }
 
   // Step t sits in buffer t & 1. The walk is unrolled by two so that each copy of the step reads
-  // a fixed buffer and its base folds into the LDS reads' immediate offsets.
-  auto step = [&](const lchar* qt) {
+  // a fixed buffer and its address folds into the LDS reads' immediate offsets.
+  // The step reading buffer qt also copies step sbn's tiles (sbn < 0: none) into nb, two copy
+  // instructions after each of the first S / dP product pairs.
+  auto step = [&](const lchar* qt, lchar* nb, int sbn) {
     const lchar* gt = qt + C::OFF_G;
+    const KVStep cp = kv_step<D>(qbase, gbase, ldbase, max(sbn, 0), N, nb);
 
     // S = Q K^T and dP = dO V^T for queries 32 h .. 32 h + 31 of the step: element i of lane
     // (ln, hf) is key 32 w + ln, query 32 h + 8 (i / 4) + 4 hf + i % 4.
@@ -431,9 +435,9 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
         sc[h][i] = 0.f;
         dp[h][i] = 0.f;
       }
-    // P = exp(s - LSE) and dS = P (dP - D) (the scale multiplies dK in the epilogue) of queries 32 h + 16 u + 8 g + 4 hf .. + 3,
-    // packed to bf16 as words 2 g, 2 g + 1 of the A operands of run u of half h (elements
-    // 8 u + 4 g .. + 3)
+    // P = exp(s - LSE) and dS = P (dP - D) of queries 32 h + 16 u + 8 g + 4 hf .. + 3 (the scale
+    // multiplies dK in the epilogue), packed to bf16 as words 2 g, 2 g + 1 of the A operands of
+    // run u of half h (elements 8 u + 4 g .. + 3)
     uint32_t wp[2][2][4], ws[2][2][4];
     auto ps_quad = [&](int h, int u, int g) {
       const int qi = 32 * h + 16 * u + 8 * g + 4 * hf;
@@ -469,6 +473,10 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       }
       sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[0], kf[s], sc[h], 0, 0, 0);
       dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[1], vf[s], dp[h], 0, 0, 0);
+      if (2 * n < NPART && sbn >= 0) {
+        kv_part(cp, wave, lane, doff, 2 * n, KVDma<D>::PW, C::OFF_G, C::OFF_L);
+        if (2 * n + 1 < NPART) kv_part(cp, wave, lane, doff, 2 * n + 1, KVDma<D>::PW, C::OFF_G, C::OFF_L);
+      }
       // half 0's P and dS under half 1's products (four quads over its SS steps)
       if (h == 1 && (s % (SS / 4)) == (SS / 4) - 1) {
         const int qd = s / (SS / 4);
@@ -480,49 +488,55 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
     }
 
     // phases C and D: dV += P^T dO and dK += dS^T Q, item j = (h, u, channel tile c); the
-    // transposed operands of item j + 1 are read while the products of item j run
-    constexpr int NC = D / 32;
-    bf16x8 cg = tr_read<C::ROWB>(gt, toff[0], 0), cq = tr_read<C::ROWB>(qt, toff[0], 0);
+    // transposed operands of item j + PD are read while the products of item j run (PD items of
+    // LDS latency covered; phase B, not these phases, sets the register peak)
+    constexpr int NC = D / 32, NJ = 4 * NC, PD = 2;
+    auto item_row = [](int j) { return 32 * (j / (2 * NC)) + 16 * ((j / NC) & 1); };
+    bf16x8 rg[PD + 1], rq[PD + 1];
 #pragma unroll
-    for (int j = 0; j < 4 * NC; ++j) {
+    for (int j = 0; j < PD; ++j) {
+      rg[j] = tr_read<C::ROWB>(gt, toff[j % NC], item_row(j));
+      rq[j] = tr_read<C::ROWB>(qt, toff[j % NC], item_row(j));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
       const int h = j / (2 * NC), u = (j / NC) & 1, c = j % NC;
-      bf16x8 ng = cg, nq = cq;
-      if (j + 1 < 4 * NC) {
-        const int h1 = (j + 1) / (2 * NC), u1 = ((j + 1) / NC) & 1, c1 = (j + 1) % NC;
-        ng = tr_read<C::ROWB>(gt, toff[c1], 32 * h1 + 16 * u1);
-        nq = tr_read<C::ROWB>(qt, toff[c1], 32 * h1 + 16 * u1);
+      if (j + PD < NJ) {
+        rg[(j + PD) % (PD + 1)] = tr_read<C::ROWB>(gt, toff[(j + PD) % NC], item_row(j + PD));
+        rq[(j + PD) % (PD + 1)] = tr_read<C::ROWB>(qt, toff[(j + PD) % NC], item_row(j + PD));
       }
       const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(wp[h][u][0], wp[h][u][1], wp[h][u][2], wp[h][u][3]));
       const bf16x8 sa = __builtin_bit_cast(bf16x8, make_uint4(ws[h][u][0], ws[h][u][1], ws[h][u][2], ws[h][u][3]));
-      acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, cg, acc_v[c], 0, 0, 0);
-      acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, cq, acc_k[c], 0, 0, 0);
+      acc_v[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, rg[j % (PD + 1)], acc_v[c], 0, 0, 0);
+      acc_k[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, rq[j % (PD + 1)], acc_k[c], 0, 0, 0);
       // half 1's P and dS under half 0's products (four quads over the 2 NC items of half 0)
       if (h == 0 && (j % (2 * NC / 4)) == (2 * NC / 4) - 1) {
         const int qd = j / (2 * NC / 4);
         ps_quad(1, qd >> 1, qd & 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      cg = ng;
-      cq = nq;
     }
   };
+  // the list entry of step t + 2 is read at step t, a step before its copies need it
+  int sbn = T > 1 ? sbof(1) : -1;
   for (int t = 0; t < T; t += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // step t is resident in buffer 0; both waves are done with buffer 1
-    if (t + 1 < T) SA_KV_ISSUE(t + 1)
-    step(base);
+    const int sb2 = t + 2 < T ? sbof(t + 2) : -1;
+    step(base0, base1, sbn);
+    sbn = sb2;
     if (t + 1 < T) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // step t + 1 is resident in buffer 1; both waves are done with buffer 0
-      if (t + 2 < T) SA_KV_ISSUE(t + 2)
-      step(base + C::BUF);
+      const int sb3 = t + 3 < T ? sbof(t + 3) : -1;
+      step(base1, base0, sbn);
+      sbn = sb3;
     }
   }
-#undef SA_KV_ISSUE
   __syncthreads();  // every wave is done with the last step's buffer
 
-  // epilogue: dK (times the scale) then dV, staged through LDS as [key][channel] rows. Element i of tile c: channel
-  // 32 c + ln, key 32 w + 8 (i / 4) + 4 hf + i % 4
+  // epilogue: dK (times the scale) then dV, staged through LDS as [key][channel] rows. Element i
+  // of tile c: channel 32 c + ln, key 32 w + 8 (i / 4) + 4 hf + i % 4
   for (int which = 0; which < 2; ++which) {
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -530,7 +544,7 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kr = 32 * wave + 8 * (i >> 2) + 4 * hf + (i & 3);
-        *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base + kr * C::OROW + (32 * c + ln) * 2) =
+        *reinterpret_cast<__attribute__((address_space(3))) __bf16*>(base0 + kr * C::OROW + (32 * c + ln) * 2) =
             (__bf16)(which == 0 ? acc[i] * scale : acc[i]);
       }
     }
@@ -542,7 +556,7 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       const int kr = kb * BK + r;
       if (kr < N)
         *reinterpret_cast<u32x4*>(obase + (size_t)kr * D * 2 + cc * 16) =
-            *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + r * C::OROW + cc * 16);
+            *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base0 + r * C::OROW + cc * 16);
     }
     __syncthreads();
   }
@@ -592,10 +606,7 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                      dout, o, lse, lse2p, deltap, ridx, rcnt, N, nqb, nkb, scale, c_log2, dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   using C = KVCfg<D>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, BQ>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BQ>), dim3((unsigned)(BH * nkb)), dim3(C::NT), C::LDS, stream, q, k, v,
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BQ>), dim3((unsigned)(BH * nkb)), dim3(C::NT), 0, stream, q, k, v,
                      dout, lse2p, deltap, cidx, ccnt, N, nqb, nkb, scale, c_log2, dk, dv);
   return hipGetLastError();
 }
