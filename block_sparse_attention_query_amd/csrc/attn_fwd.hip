@@ -488,6 +488,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   // so the vector units and the LDS reads run under the matrix products of one wave.
   auto scores_p = [&](const lchar* kt, f32x16 (&sn)[2], const f32x16 (&sc)[2], uint32_t (&pw)[16],
                       float (&rs)[4]) {
+    // raised priority for this phase, whose vector work bounds it: the other wave on the SIMD,
+    // usually in its P V products, then fills the matrix core around this wave's instructions
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sn[0][i] = 0.f;
@@ -514,8 +517,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     }
 #pragma unroll
     for (int j = 2 * (D / 16); j < 16; ++j) p_word(sc, j, pw, rs);
+    __builtin_amdgcn_s_setprio(0);
   };
 
+  // kept-list entries t + 1 and t + 2 of step t, in scalar registers; entry t + 3 is fetched
+  // during step t by a vector load (counted by vmcnt, which the next step's barrier drains), so
+  // that no scalar load waits right behind the barrier
+  int e1 = cnt > 1 ? blk(1) : -1, e2 = cnt > 2 ? blk(2) : -1;
+  int vl = 0, lz = 0;
+  asm volatile("" : "+v"(lz));  // a zero opaque to the compiler, which makes the list load a vector load
   auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
                   auto next_tag) {
     constexpr int NEXT = decltype(next_tag)::value;
@@ -523,8 +533,19 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
     // the DMA for K(t+2) and V(t+1) is issued behind the score MFMAs, so that the waves released
     // by the barrier start on the matrix cores instead of queueing their copies first
-    const int blk2 = t + 2 < cnt ? blk(t + 2) : -1;
-    const int blk1 = t + 1 < cnt ? blk(t + 1) : -1;
+    int blk1, blk2;
+    if constexpr (WIN) {
+      blk2 = t + 2 < cnt ? blk(t + 2) : -1;
+      blk1 = t + 1 < cnt ? blk(t + 1) : -1;
+    } else {
+      if (t > 0) {
+        e1 = e2;
+        e2 = t + 2 < cnt ? min(max(__builtin_amdgcn_readfirstlane(vl), 0), nkb - 1) : -1;
+      }
+      if (t + 3 < cnt) vl = list[t + 3 + lz];
+      blk1 = e1;
+      blk2 = e2;
+    }
     uint32_t pw[16];
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (NEXT != 0) {
