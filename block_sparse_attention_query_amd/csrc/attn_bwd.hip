@@ -158,21 +158,40 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
     for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
 
   // Block t of the list sits in buffer t & 1. The walk is unrolled by two so that each copy of the
-  // step reads a fixed buffer and its base folds into the LDS reads' immediate offsets.
-  auto step = [&](int t, const lchar* kt) {
+  // step reads a fixed buffer and its base folds into the LDS reads' immediate offsets. The list
+  // entries of blocks t and t + 1 are in scalar registers at step t; entry t + 2 is fetched during
+  // step t by a vector load (counted by vmcnt, not by the lgkmcnt that the LDS reads wait on).
+  int e0 = cnt > 0 ? blk(0) : 0, e1 = cnt > 1 ? blk(1) : -1;
+  int vl = 0, lz = 0;
+  asm volatile("" : "+v"(lz));  // a zero opaque to the compiler, which makes the list load a vector load
+  auto step = [&](int t, const lchar* kt, lchar* nb) {
     const lchar* vt = kt + C::TILE;
-    const int kb = blk(t);
+    const int kb = e0, kn = e1;
+    if (t + 2 < cnt) vl = list[t + 2 + lz];
     f32x16 s0 = {}, s1 = {}, p0 = {}, p1 = {};
+    // operands of channel slice s + 1 are read while the products of slice s run
+    bf16x8 ra[2][4];
+    auto rd = [&](int s, bf16x8 (&r)[4]) {
+      r[0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s]);
+      r[1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s] + 32 * C::ROWB);
+      r[2] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s]);
+      r[3] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s] + 32 * C::ROWB);
+    };
+    rd(0, ra[0]);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s]);
-      const bf16x8 a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koff[s] + 32 * C::ROWB);
-      const bf16x8 b0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s]);
-      const bf16x8 b1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vt + koff[s] + 32 * C::ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, gf[s], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, gf[s], p1, 0, 0, 0);
+      if (s + 1 < D / 16) rd(s + 1, ra[(s + 1) & 1]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s & 1][0], qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s & 1][1], qf[s], s1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s & 1][2], gf[s], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[s & 1][3], gf[s], p1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keeps the reads of slice s + 1 ahead of these products
+    }
+    // block t + 1 into the other buffer, issued behind the products so that the waves released by
+    // the barrier start on the matrix cores
+    if (kn >= 0) {
+      dma_tile_rsrc<D, BQ>(kbase, kn, N, wave, doff, nb);
+      dma_tile_rsrc<D, BQ>(vbase, kn, N, wave, doff, nb + C::TILE);
     }
     if (kb * BK + BK > N) {  // ragged last key block: keys past N take no part
 #pragma unroll
@@ -186,7 +205,10 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
         s1[i] = b;
       }
     }
-    // dS^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t
+    // dS^T as the B operand: key chunk c = 2 t + u takes elements 8u .. 8u+7 of tile t. This
+    // vector-bound phase runs at raised priority, so that the other wave on the SIMD fills the
+    // matrix core around it.
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 db[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -206,29 +228,24 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_bwd_dq_kernel(
       db[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
       db[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
     }
+    __builtin_amdgcn_s_setprio(0);
     // dQ^T (channels x queries) += K^T (channels x keys) dS^T (keys x queries)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int r = 0; r < D / 32; ++r)
         acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<C::ROWB>(kt, toff[r], 16 * c), db[c], acc[r], 0, 0, 0);
+    e0 = e1;
+    e1 = t + 2 < cnt ? min(max(__builtin_amdgcn_readfirstlane(vl), 0), nkb - 1) : -1;
   };
   for (int t = 0; t < cnt; t += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block t is resident in buffer 0; every wave is done with buffer 1
-    if (t + 1 < cnt) {
-      dma_tile_rsrc<D, BQ>(kbase, blk(t + 1), N, wave, doff, buf1);
-      dma_tile_rsrc<D, BQ>(vbase, blk(t + 1), N, wave, doff, buf1 + C::TILE);
-    }
-    step(t, buf0);
+    step(t, buf0, buf1);
     if (t + 1 < cnt) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // block t + 1 is resident in buffer 1; every wave is done with buffer 0
-      if (t + 2 < cnt) {
-        dma_tile_rsrc<D, BQ>(kbase, blk(t + 2), N, wave, doff, buf0);
-        dma_tile_rsrc<D, BQ>(vbase, blk(t + 2), N, wave, doff, buf0 + C::TILE);
-      }
-      step(t + 1, buf1);
+      step(t + 1, buf1, buf0);
     }
   }
   __syncthreads();
@@ -517,20 +534,24 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the list entry of step t + 2 is read at step t, a step before its copies need it
+  // The list entry of step t + 2 is fetched during step t by a vector load (counted by vmcnt, not
+  // by the lgkmcnt that the LDS reads wait on) and moved to a scalar register after the step.
+  int vl = 0, lz = 0;
+  asm volatile("" : "+v"(lz));  // a zero opaque to the compiler, which makes the list load a vector load
+  auto sb_at = [&](int t, int entry) { return min(max(entry, 0), nqb - 1) * SPB + t % SPB; };
   int sbn = T > 1 ? sbof(1) : -1;
   for (int t = 0; t < T; t += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // step t is resident in buffer 0; both waves are done with buffer 1
-    const int sb2 = t + 2 < T ? sbof(t + 2) : -1;
+    if (t + 2 < T) vl = list[(t + 2) / SPB + lz];
     step(base0, base1, sbn);
-    sbn = sb2;
+    sbn = t + 2 < T ? sb_at(t + 2, __builtin_amdgcn_readfirstlane(vl)) : -1;
     if (t + 1 < T) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // step t + 1 is resident in buffer 1; both waves are done with buffer 0
-      const int sb3 = t + 3 < T ? sbof(t + 3) : -1;
+      if (t + 3 < T) vl = list[(t + 3) / SPB + lz];
       step(base1, base0, sbn);
-      sbn = sb3;
+      sbn = t + 3 < T ? sb_at(t + 3, __builtin_amdgcn_readfirstlane(vl)) : -1;
     }
   }
   __syncthreads();  // every wave is done with the last step's buffer
