@@ -4,7 +4,8 @@
 One step = the whole path over one batch of synthetic input already resident in HBM:
     sparse_attn_pool_qk      block mean pooling of Q and K
     sparse_attn_select_mask  pooled softmax, hybrid Top-k U Top-p mask and kept-block lists
-    sparse_attn_fwd_lists    block-sparse flash attention over the kept blocks
+    sparse_attn_row_order    the rows' work order (longest kept lists first on short grids)
+    sparse_attn_fwd_lists_ordered  block-sparse flash attention over the kept blocks
 on the Wan2.1-14B 720p-shaped workload (40 heads x 75600 tokens x 128, bf16, Bq=128, Bk=64,
 k_frac=0.03, p=0.9). Throughput is executed TFLOP/s: 4 d sum over kept (query block, key block)
 pairs of valid queries x valid keys, divided by the step time.
@@ -528,6 +529,7 @@ def main(argv=None):
            "mask": torch.empty((B, H, nqb, nkb), dtype=torch.uint8, device=dev),
            "kept_idx": torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=dev),
            "kept_cnt": torch.empty((B, H, nqb), dtype=torch.int32, device=dev)}
+    order = torch.empty(B * H * nqb, dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     if args.pattern != "hybrid":
         print(json.dumps(pattern_bench(args, sa, w, q, k, v, gen_s)), flush=True)
@@ -550,9 +552,10 @@ def main(argv=None):
         if ev is not None:
             ev[1].record()
         sa.select_mask(qp, kp, w.k_frac, w.p, kept_lists=True, out=sel)
+        sa.row_order(sel["kept_cnt"], out=order)
         if ev is not None:
             ev[2].record()
-        sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, out=o)
+        sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, out=o, row_order=order)
         if ev is not None:
             ev[3].record()
 
@@ -578,7 +581,7 @@ def main(argv=None):
     pool_ms, select_ms, attn_ms = (float(v) for v in per.mean(axis=0))
     stats = {name: {"median": round(float(np.median(col)), 4), "p10": round(float(np.percentile(col, 10)), 4),
                     "p90": round(float(np.percentile(col, 90)), 4)}
-             for name, col in zip(("pool_qk", "select_mask", "fwd_lists"), per.T)}
+             for name, col in zip(("pool_qk", "select_mask+row_order", "fwd_lists"), per.T)}
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     alg_bytes = 4 * B * H * N * d * q.element_size()  # Q, K, V read once and O written once
@@ -602,7 +605,7 @@ def main(argv=None):
                    "k_frac": w.k_frac, "p": w.p, "kept_block_density": round(density, 5),
                    "block_sparsity": round(1 - density, 5), "executed_tflop_per_step": round(flops / 1e12, 4),
                    "parallelism": "none (1 GPU)"},
-        "ms_per_call": {"pool_qk": round(pool_ms, 4), "select_mask": round(select_ms, 4),
+        "ms_per_call": {"pool_qk": round(pool_ms, 4), "select_mask+row_order": round(select_ms, 4),
                         "fwd_lists": round(attn_ms, 4)},
         "ms_per_call_stats": stats,
         "tile_tflop_per_step": round(tile_flops / 1e12, 4),

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA_PAT_MULTIDIAG,  # noqa: F401
                    SA_PAT_STRIPE, SparseAttnError)
 
-__all__ = ["pool_qk", "select_mask", "fwd", "fwd_noalloc", "fwd_lists", "fwd_workspace_size", "bwd", "bwd_workspace_size",
+__all__ = ["pool_qk", "select_mask", "fwd", "fwd_noalloc", "fwd_lists", "row_order", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
            "window_transpose", "squad_fwd", "squad_attention", "topk_count", "sparse_attention", "probe_correct",
            "probe_workspace_size", "kmeans", "cluster_select", "permute_rows", "cluster_fwd", "svg2_attention",
@@ -163,14 +163,28 @@ def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.T
     return o, lse
 
 
+def row_order(kept_cnt: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Work order of the attention rows for ``fwd_lists(..., row_order=...)`` (int32, one entry
+    per row of ``kept_cnt``): longest lists first within each XCD on short grids, the kernels'
+    default order otherwise. Scheduling only."""
+    if kept_cnt.dtype != torch.int32 or kept_cnt.dim() != 3 or not kept_cnt.is_contiguous() or not kept_cnt.is_cuda:
+        raise ValueError("kept_cnt must be a contiguous int32 [B, H, nqb] device tensor")
+    B, H, nqb = kept_cnt.shape
+    order = torch.empty(B * H * nqb, dtype=torch.int32, device=kept_cnt.device) if out is None else \
+        _check_out(out, (B * H * nqb,), torch.int32, kept_cnt.device)
+    _lib.check(_lib.lib().sparse_attn_row_order(kept_cnt.data_ptr(), B, H, nqb, order.data_ptr(), _stream(kept_cnt)))
+    return order
+
+
 def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor, kept_cnt: torch.Tensor,
               bq: int, bk: int = 64, scale: float | None = None, return_lse: bool = False,
-              out: torch.Tensor | None = None, window: int | None = None):
+              out: torch.Tensor | None = None, window: int | None = None, row_order: torch.Tensor | None = None):
     """Block-sparse attention from kept-block lists (as written by ``select_mask(kept_lists=True)``).
 
     With ``window``, the attention runs over the window-transposed token order (the lists index
     its blocks) while q, k, v and the output stay in the original order: the same result as
-    ``window_transpose`` of the inputs, ``fwd_lists`` and the inverse transpose of the output."""
+    ``window_transpose`` of the inputs, ``fwd_lists`` and the inverse transpose of the output.
+    ``row_order`` (from ``row_order``) sets the rows' work order; the result is unchanged."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     nqb, nkb = _nblocks(N, bq), _nblocks(N, bk)
@@ -183,7 +197,17 @@ def fwd_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_idx: torch
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
-    if window is None:
+    if row_order is not None:
+        if window is not None:
+            raise ValueError("row_order applies to the plain token order only")
+        if row_order.dtype != torch.int32 or tuple(row_order.shape) != (B * H * nqb,) or \
+                not row_order.is_contiguous() or row_order.device != q.device:
+            raise ValueError(f"row_order must be a contiguous int32 [{B * H * nqb}] tensor on the device of q")
+        _lib.check(_lib.lib().sparse_attn_fwd_lists_ordered(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], kept_idx.data_ptr(), kept_cnt.data_ptr(),
+            row_order.data_ptr(), B, H, N, d, bq, bk, scale, o.data_ptr(), None if lse is None else lse.data_ptr(),
+            _stream(q)))
+    elif window is None:
         _lib.check(_lib.lib().sparse_attn_fwd_lists(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), _DTYPES[q.dtype], kept_idx.data_ptr(), kept_cnt.data_ptr(), B,
             H, N, d, bq, bk, scale, o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q)))

@@ -29,6 +29,8 @@ SIGNATURES = {
     "sparse_attn_fwd_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_fwd_lists": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_fwd_lists_window": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
+    "sparse_attn_row_order": (_i, [_vp, _i, _i, _i, _vp, _vp]),
+    "sparse_attn_fwd_lists_ordered": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp]),
     "sparse_attn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "sparse_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _d, _vp, _vp, _vp, _vp, _sz,
                              _vp]),

@@ -21,7 +21,8 @@ hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, in
 hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx, int32_t* kcnt, hipStream_t stream);
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
                        const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
-                       hipStream_t stream);
+                       hipStream_t stream, const int32_t* row_order = nullptr);
+hipError_t launch_row_order(const int32_t* kcnt, int rows, int32_t* order, hipStream_t stream);
 hipError_t launch_attn_window(const void* q, const void* k, const void* v, const int32_t* kidx, const int32_t* kcnt,
                               int BH, int N, int d, int Bq, double scale, int window, void* o, float* lse,
                               hipStream_t stream);
@@ -191,6 +192,25 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
   return hip_status(sa::launch_attn(q, k, v, dtype, kept_idx, kept_cnt, B * H, N, d, Bq, scale, o, lse,
                                     static_cast<hipStream_t>(stream)),
                     "fwd_lists: attention launch");
+}
+
+int sparse_attn_row_order(const int32_t* kept_cnt, int B, int H, int nqb, int32_t* order, void* stream) {
+  if (!kept_cnt || !order) return fail(SA_ERR_INVALID_ARG, "row_order: null pointer");
+  if (B <= 0 || H <= 0 || nqb <= 0) return fail(SA_ERR_INVALID_ARG, "row_order: B, H and nqb must be positive");
+  if ((long long)B * H * nqb > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "row_order: too many rows");
+  return hip_status(sa::launch_row_order(kept_cnt, B * H * nqb, order, static_cast<hipStream_t>(stream)),
+                    "row_order: launch");
+}
+
+int sparse_attn_fwd_lists_ordered(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                                  const int32_t* kept_cnt, const int32_t* row_order, int B, int H, int N, int d,
+                                  int Bq, int Bk, double scale, void* o, float* lse, void* stream) {
+  if (!kept_idx || !kept_cnt || !row_order) return fail(SA_ERR_INVALID_ARG, "fwd_lists_ordered: null pointer");
+  int rc = check_fwd_common(q, k, v, dtype, B, H, N, d, Bq, Bk, scale, o);
+  if (rc) return rc;
+  return hip_status(sa::launch_attn(q, k, v, dtype, kept_idx, kept_cnt, B * H, N, d, Bq, scale, o, lse,
+                                    static_cast<hipStream_t>(stream), row_order),
+                    "fwd_lists_ordered: attention launch");
 }
 
 int sparse_attn_fwd_lists_window(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,

@@ -63,14 +63,15 @@ template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
-    float* __restrict__ o, float* __restrict__ lse) {
+    float* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ row_order) {
   constexpr int NT = BQ * 2;
   constexpr int HK = 32;     // keys per LDS stage
   constexpr int KP = D + 1;  // padded K row (floats)
   __shared__ float ks[HK * KP];
   __shared__ __attribute__((aligned(16))) float vs[HK * D];
 
-  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
+  const int tile = row_order ? min(max(row_order[blockIdx.x], 0), (int)gridDim.x - 1)
+                            : xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
   const int wave = threadIdx.x >> 6;
@@ -242,7 +243,8 @@ template <int D, int BQ, bool WT = false, bool WIN = false>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
-    void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w, int win) {
+    void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w, int win,
+    const int32_t* __restrict__ row_order) {
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
@@ -251,7 +253,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   lchar* const vb0 = (lchar*)vbuf_;
   lchar* const vb1 = vb0 + C::TILE;
 
-  const int tile = xcd_chunk_row(blockIdx.x, gridDim.x);
+  // row_order (optional): the row of each workgroup; entries are clamped to the grid
+  const int tile = row_order ? min(max(row_order[blockIdx.x], 0), (int)gridDim.x - 1)
+                            : xcd_chunk_row(blockIdx.x, gridDim.x);
   const int bh = tile / nqb;
   const int qb = tile - bh * nqb;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: SGPR
@@ -639,30 +643,66 @@ hipError_t launch_compact(const uint8_t* mask, int rows, int nkb, int32_t* kidx,
   return hipGetLastError();
 }
 
+// Launch order of the attention rows: order[w] is the row that workgroup w computes. Workgroups
+// reach XCD w % 8 in order of w, each XCD walking its rows in the order xcd_chunk_row gives.
+// Over a grid of many rounds that order stays (its chunks keep neighbouring rows, and the key
+// blocks they share, within one XCD's L2). Over a short grid (fewer than kLptRows rows, under 16
+// rounds of the 512 workgroups that fit the chip) the last round's rows decide the time, so each
+// XCD takes its rows longest list first (equal lengths in the default order): workgroup 8 l + x
+// gets the row of rank l among XCD x's rows, ranked by descending count. Rows past the whole
+// XCD shares keep their default place.
+constexpr int kLptRows = 8192;
+__global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ kcnt, int rows,
+                                                         int32_t* __restrict__ order) {
+  const int per = rows >> 3;
+  if (rows >= kLptRows) {
+    for (int w = blockIdx.x * 1024 + threadIdx.x; w < rows; w += gridDim.x * 1024) order[w] = xcd_chunk_row(w, rows);
+    return;
+  }
+  __shared__ int cl[kLptRows / 8];
+  const int x = blockIdx.x;
+  for (int l = threadIdx.x; l < per; l += 1024) cl[l] = kcnt[xcd_chunk_row(8 * l + x, rows)];
+  __syncthreads();
+  for (int l = threadIdx.x; l < per; l += 1024) {
+    const int c = cl[l];
+    int rank = 0;
+    for (int j = 0; j < per; ++j) rank += (cl[j] > c) | ((cl[j] == c) & (j < l));
+    order[8 * rank + x] = xcd_chunk_row(8 * l + x, rows);
+  }
+  if (x == 0)
+    for (int w = per * 8 + threadIdx.x; w < rows; w += 1024) order[w] = w;
+}
+
+hipError_t launch_row_order(const int32_t* kcnt, int rows, int32_t* order, hipStream_t stream) {
+  const unsigned grid = rows >= kLptRows ? (unsigned)((rows + 1023) / 1024) : 8u;
+  hipLaunchKernelGGL(row_order_kernel, dim3(grid), dim3(1024), 0, stream, kcnt, rows, order);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int BQ>
 static hipError_t launch_attn_t(const void* q, const void* k, const void* v, const int32_t* kidx,
                                 const int32_t* kcnt, int BH, int N, int nqb, int nkb, float c_log2, void* o,
-                                float* lse, hipStream_t stream) {
+                                float* lse, const int32_t* row_order, hipStream_t stream) {
   if constexpr (DT == kBF16) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
-                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0, 0);
+                       q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0, 0, row_order);
   } else {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(BQ * 2), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), kidx,
-                       kcnt, N, nqb, nkb, c_log2, static_cast<float*>(o), lse);
+                       kcnt, N, nqb, nkb, c_log2, static_cast<float*>(o), lse, row_order);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype, const int32_t* kidx,
                        const int32_t* kcnt, int BH, int N, int d, int Bq, double scale, void* o, float* lse,
-                       hipStream_t stream) {
+                       hipStream_t stream, const int32_t* row_order) {
   const int nqb = (N + Bq - 1) / Bq;
   const int nkb = (N + BK - 1) / BK;
   const float c_log2 = (float)(scale * 1.4426950408889634);
 #define SA_ATTN_CASE(DT_, D_, BQ_)                                                               \
   if (dtype == DT_ && d == D_ && Bq == BQ_)                                                      \
-    return launch_attn_t<DT_, D_, BQ_>(q, k, v, kidx, kcnt, BH, N, nqb, nkb, c_log2, o, lse, stream);
+    return launch_attn_t<DT_, D_, BQ_>(q, k, v, kidx, kcnt, BH, N, nqb, nkb, c_log2, o, lse, row_order, stream);
   SA_ATTN_CASE(kBF16, 128, 128)
   SA_ATTN_CASE(kBF16, 128, 64)
   SA_ATTN_CASE(kBF16, 64, 128)
@@ -685,7 +725,7 @@ hipError_t launch_attn_window(const void* q, const void* k, const void* v, const
 #define SA_WT_CASE(D_, BQ_)                                                                                  \
   if (d == D_ && Bq == BQ_) {                                                                                \
     hipLaunchKernelGGL((attn_fwd_kernel<D_, BQ_, true>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D_, BQ_>::NT), 0, \
-                       stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, nw, window, 0);            \
+                       stream, q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, nw, window, 0, nullptr);   \
     return hipGetLastError();                                                                                \
   }
   SA_WT_CASE(128, 128)
@@ -705,7 +745,7 @@ static hipError_t launch_squad_t(const void* q, const void* k, const void* v, in
   const int nw = WT ? N / window : 0;
   const int32_t* none = nullptr;
   hipLaunchKernelGGL((attn_fwd_kernel<D, BQ, WT, true>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
-                     q, k, v, none, none, N, nqb, nkb, c_log2, o, lse, nw, WT ? window : 0, WT ? nw : window);
+                     q, k, v, none, none, N, nqb, nkb, c_log2, o, lse, nw, WT ? window : 0, WT ? nw : window, none);
   return hipGetLastError();
 }
 

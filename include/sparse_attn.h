@@ -157,6 +157,28 @@ int sparse_attn_fwd_lists(const void* q, const void* k, const void* v, int dtype
                           void* o, float* lse, void* stream);
 
 /*
+ * Work order of the attention rows for sparse_attn_fwd_lists_ordered: which row (b, h, query
+ * block) each workgroup computes. Scheduling only; it changes no result.
+ *   kept_cnt   device, [B, H, nqb] int32 (as sparse_attn_select_mask writes it).
+ *   order      device out, [B * H * nqb] int32, a permutation of the rows.
+ * Workgroups reach the chip's eight XCDs round-robin. With B * H * nqb >= 8192 (at least 16
+ * rounds of the 512 workgroups that run at once) the order is the default one of the kernels,
+ * which keeps neighbouring rows of a head in one XCD's L2; below that each XCD takes its rows
+ * longest list first (ties in the default order), which shortens the last round.
+ * Errors: SA_ERR_INVALID_ARG for null pointers or non-positive sizes.
+ */
+int sparse_attn_row_order(const int32_t* kept_cnt, int B, int H, int nqb, int32_t* order, void* stream);
+
+/*
+ * sparse_attn_fwd_lists with workgroup w computing row row_order[w] (from sparse_attn_row_order;
+ * entries are clamped to the row range, and an order that is not a permutation leaves rows
+ * uncomputed or computed twice). Results equal those of sparse_attn_fwd_lists bit for bit.
+ */
+int sparse_attn_fwd_lists_ordered(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
+                                  const int32_t* kept_cnt, const int32_t* row_order, int B, int H, int N, int d,
+                                  int Bq, int Bk, double scale, void* o, float* lse, void* stream);
+
+/*
  * sparse_attn_fwd_lists over the window-transposed token order without materialising it: the
  * attention's rows (queries and keys alike) are those of sparse_attn_window_transpose's forward
  * order, row s being token (s mod nw) * window + s / nw with nw = N / window, while q, k, v, o

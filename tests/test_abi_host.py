@@ -42,7 +42,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -137,6 +137,35 @@ def _fwd_lists(**kw):
 ])
 def test_fwd_lists_rejects(kw, code):
     assert _fwd_lists(**kw) == code
+
+
+def _row_order(**kw):
+    a = dict(cnt=P, B=1, H=2, nqb=16, order=P, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_row_order(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cnt=None), -1), (dict(order=None), -1), (dict(B=0), -1), (dict(H=-1), -1), (dict(nqb=0), -1),
+    (dict(B=1 << 16, H=1 << 16, nqb=2), -2),
+])
+def test_row_order_rejects(kw, code):
+    assert _row_order(**kw) == code
+
+
+def _fwd_lists_ordered(**kw):
+    a = dict(q=P, k=P, v=P, dtype=0, idx=P, cnt=P, order=P, B=1, H=2, N=1024, d=64, Bq=64, Bk=64, scale=0.125, o=P,
+             lse=None, stream=None)
+    a.update(kw)
+    return _lib.lib().sparse_attn_fwd_lists_ordered(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(order=None), -1), (dict(idx=None), -1), (dict(cnt=None), -1), (dict(v=None), -1), (dict(d=48), -2),
+    (dict(Bq=32), -2), (dict(o=P_ODD), -1), (dict(scale=0.0), -1),
+])
+def test_fwd_lists_ordered_rejects(kw, code):
+    assert _fwd_lists_ordered(**kw) == code
 
 
 def _fwd_lists_window(**kw):
