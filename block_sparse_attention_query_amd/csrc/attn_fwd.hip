@@ -415,42 +415,6 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       m_run = m_new;
     }
   };
-  // P^T of the block (B operand of the PV product) and its row sum; key chunk c = 2 t + u takes
-  // elements 8u .. 8u+7 of tile t, and the row sum adds the same bf16 values the product uses.
-  // Then O^T += V^T P^T with V^T fragments read from the tile vt by transpose reads.
-  auto accumulate = [&](const f32x16 (&sc)[2], lchar* vt) {
-    bf16x8 pb[4];
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      uint32_t w0[4], w1[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e + 1], c_log2, -m_run)));
-        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e + 1], c_log2, -m_run)));
-        rs[(e & 1) * 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs[(e & 1) * 2], false);
-        rs[(e & 1) * 2 + 1] =
-            __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs[(e & 1) * 2 + 1], false);
-      }
-      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
-      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
-    }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < D / 32; ++r) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
-        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
-      }
-  };
-
   const bool ragged_last = cnt > 0 && (N % BK) != 0 && blk(cnt - 1) == nkb - 1;
   // Step t. NEXT: 0 = no block t + 1 (last step), 1 = full block t + 1, 2 = ragged block t + 1.
   // kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1).
@@ -467,31 +431,43 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     rs[(e & 1) * 2 + h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]), ones,
                                                           rs[(e & 1) * 2 + h], false);
   };
-  // O^T += V^T P^T for the packed words of the block in vt
-  auto pv = [&](const uint32_t (&pw)[16], lchar* vt) {
+  // V^T fragments of key chunk c, channel tile r, from the tile vt (two transpose reads)
+  auto vrd = [&](lchar* vt, int c, int r) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // O^T += V^T P^T for the packed words of the block in vt; va holds chunk 0's fragments, read
+  // earlier, and chunk c + 1 is read while chunk c multiplies
+  auto pv = [&](const uint32_t (&pw)[16], lchar* vt, bf16x8 (&va0)[D / 32]) {
     bf16x8 pb[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pb[u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u], pw[8 * u + 2], pw[8 * u + 4], pw[8 * u + 6]));
       pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u + 1], pw[8 * u + 3], pw[8 * u + 5], pw[8 * u + 7]));
     }
+    bf16x8 va[2][D / 32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int r = 0; r < D / 32; ++r) va[0][r] = va0[r];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int r = 0; r < D / 32; ++r) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
-        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
+        if (c + 1 < 4) va[(c + 1) & 1][r] = vrd(vt, c + 1, r);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c & 1][r], pb[c], oacc[r], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (c + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+    }
   };
   // S^T of the key block in kt into sn, interleaved with the P words of sc: each pair of score
   // MFMAs is followed by two P words, and the K fragments are read two steps ahead (three slots),
-  // so the vector units and the LDS reads run under the matrix products of one wave.
+  // so the vector units and the LDS reads run under the matrix products of one wave. mid(s) runs
+  // after s-step s (the step's copies).
   auto scores_p = [&](const lchar* kt, f32x16 (&sn)[2], const f32x16 (&sc)[2], uint32_t (&pw)[16],
-                      float (&rs)[4]) {
+                      float (&rs)[4], auto&& mid) {
     // raised priority for this phase, whose vector work bounds it: the other wave on the SIMD,
     // usually in its P V products, then fills the matrix core around this wave's instructions
     __builtin_amdgcn_s_setprio(1);
@@ -518,6 +494,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s % 3], qf[s], sn[1], 0, 0, 0);
       if (2 * s + 1 < 16) p_word(sc, 2 * s + 1, pw, rs);
       __builtin_amdgcn_sched_barrier(0);
+      mid(s);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 2 * (D / 16); j < 16; ++j) p_word(sc, j, pw, rs);
@@ -535,7 +513,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     constexpr int NEXT = decltype(next_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
-    // the DMA for K(t+2) and V(t+1) is issued behind the score MFMAs, so that the waves released
+    // the DMA for K(t+2) and V(t+1) is issued between the score MFMAs, so that the waves released
     // by the barrier start on the matrix cores instead of queueing their copies first
     int blk1, blk2;
     if constexpr (WIN) {
@@ -552,18 +530,33 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     }
     uint32_t pw[16];
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    auto issue_all = [&]() {
+      if (blk2 >= 0) copy(kbase, blk2, kf);
+      if (blk1 >= 0) copy(vbase, blk1, vf);
+    };
+    // the copies go out between score products: K after the second pair of s-steps' products, V
+    // after three quarters of them, so their issue hides under the matrix core instead of delaying
+    // the first P V products
+    auto issue = [&](int s) {
+      if (s == 1 && blk2 >= 0) copy(kbase, blk2, kf);
+      if (s == 3 * (D / 64) - 1 && blk1 >= 0) copy(vbase, blk1, vf);
+    };
     if constexpr (NEXT != 0) {
-      scores_p(kn, sn, sc, pw, rs);
+      scores_p(kn, sn, sc, pw, rs, issue);
       if constexpr (NEXT == 2) mask_tail(sn, blk1);
       if constexpr (WIN) mask_win(sn, blk1);
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) p_word(sc, j, pw, rs);
     }
-    if (blk2 >= 0) copy(kbase, blk2, kf);
-    if (blk1 >= 0) copy(vbase, blk1, vf);
+    // the first V^T fragments are read before anything else of the P V half is issued
+    bf16x8 va0[D / 32];
+#pragma unroll
+    for (int r = 0; r < D / 32; ++r) va0[r] = vrd(vc, 0, r);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT == 0) issue_all();
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-    pv(pw, vc);
+    pv(pw, vc, va0);
     if constexpr (NEXT != 0) raise_max(block_max(sn));
   };
 
