@@ -439,26 +439,28 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
         reinterpret_cast<__attribute__((address_space(3))) v4i16*>(vt + voff[r][1] + c * 16 * C::ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // O^T += V^T P^T for the packed words of the block in vt; va holds chunk 0's fragments, read
-  // earlier, and chunk c + 1 is read while chunk c multiplies
-  auto pv = [&](const uint32_t (&pw)[16], lchar* vt, bf16x8 (&va0)[D / 32]) {
+  // O^T += V^T P^T for the packed words of the block in vt; va0 holds the fragments of key chunks 0
+  // and 1, read earlier, and chunk c + 2 is read while chunk c multiplies
+  auto pv = [&](const uint32_t (&pw)[16], lchar* vt, bf16x8 (&va0)[2][D / 32]) {
     bf16x8 pb[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pb[u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u], pw[8 * u + 2], pw[8 * u + 4], pw[8 * u + 6]));
       pb[2 + u] = __builtin_bit_cast(bf16x8, make_uint4(pw[8 * u + 1], pw[8 * u + 3], pw[8 * u + 5], pw[8 * u + 7]));
     }
-    bf16x8 va[2][D / 32];
+    bf16x8 va[3][D / 32];
 #pragma unroll
-    for (int r = 0; r < D / 32; ++r) va[0][r] = va0[r];
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) va[a][r] = va0[a][r];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int r = 0; r < D / 32; ++r) {
-        if (c + 1 < 4) va[(c + 1) & 1][r] = vrd(vt, c + 1, r);
-        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c & 1][r], pb[c], oacc[r], 0, 0, 0);
+        if (c + 2 < 4) va[(c + 2) % 3][r] = vrd(vt, c + 2, r);
+        oacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c % 3][r], pb[c], oacc[r], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (c + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (c + 2 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
   };
@@ -549,10 +551,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) p_word(sc, j, pw, rs);
     }
-    // the first V^T fragments are read before anything else of the P V half is issued
-    bf16x8 va0[D / 32];
+    // the V^T fragments of the first two key chunks are read before anything else of the P V half
+    bf16x8 va0[2][D / 32];
 #pragma unroll
-    for (int r = 0; r < D / 32; ++r) va0[r] = vrd(vc, 0, r);
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < D / 32; ++r) va0[a][r] = vrd(vc, a, r);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT == 0) issue_all();
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
