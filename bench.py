@@ -64,8 +64,13 @@ def executed_flops(mask_cpu, n, bq, bk, d):
     return float(4 * d * (m * nq[:, None] * nk[None, :]).sum())
 
 
-def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
-    """The float64 oracle on a bounded sample of the same workload, on the host cores."""
+def cpu_baseline(w, x, mask_cpu, sample_blocks: int, o_head0=None, lse_head0=None):
+    """The float64 oracle on a bounded sample of the same workload, on the host cores.
+
+    With the GPU's output for head 0 (``o_head0`` [B, 1, N, d], ``lse_head0`` [B, 1, N]) it also
+    returns the parity of the timed call on that sample: the head's mask against the oracle's
+    (mismatches and ties within 1e-6, as the parity tests classify them) and the attention error
+    on the sampled query blocks whose mask rows agree."""
     import numpy as np
     import oracle
     try:
@@ -80,7 +85,7 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
     nqb = mask_cpu.shape[2]
     scale = 1.0 / math.sqrt(w.head_dim)
     t0 = time.perf_counter()
-    mask_o, _ = oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, scale)
+    mask_o, info = oracle.block_mask(q, k, w.bq, w.bk, w.k_frac, w.p, scale)
     t_mask = time.perf_counter() - t0
     t_mask_1t = None
     if threadpool_limits is not None:
@@ -90,7 +95,7 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
             t_mask_1t = time.perf_counter() - t0
     blocks = sorted(set(np.linspace(0, nqb - 1, sample_blocks).round().astype(int).tolist()))
     t0 = time.perf_counter()
-    oracle.masked_attention(q, k, v, mask_o, w.bq, w.bk, blocks=[(0, 0, i) for i in blocks])
+    ro, rl = oracle.masked_attention(q, k, v, mask_o, w.bq, w.bk, blocks=[(0, 0, i) for i in blocks])
     t_attn = time.perf_counter() - t0
     sub = np.zeros_like(mask_o)
     sub[0, 0, blocks] = mask_o[0, 0, blocks]
@@ -99,7 +104,28 @@ def cpu_baseline(w, x, mask_cpu, sample_blocks: int):
     # whole call on all heads: the mask oracle per head, attention scaled by executed FLOPs
     full_flops = executed_flops(mask_cpu, w.tokens, w.bq, w.bk, w.head_dim)
     extrapolated = w.batch * w.heads * t_mask + t_attn * full_flops / flops
-    return {
+    parity = None
+    if o_head0 is not None:
+        gm = mask_cpu[:, h:h + 1]
+        rep = oracle.compare_masks(info["probs"], mask_o, gm, w.k_frac, w.p)
+        same = (gm == mask_o).all(axis=-1)[0, 0]
+        rows = np.zeros(w.tokens, dtype=bool)
+        for i in blocks:
+            if same[i]:
+                rows[i * w.bq:min(w.tokens, (i + 1) * w.bq)] = True
+        go = o_head0[0, 0].double().numpy()[rows]
+        err = np.abs(go - ro[0, 0][rows])
+        parity = {"head": h, "mask_rows": rep["rows"], "mask_rows_equal": rep["rows_equal"],
+                  "mask_ties": rep["ties"], "mask_mismatches": rep["mismatches"],
+                  "attn_rows": int(rows.sum()), "attn_max_abs": float(err.max()) if err.size else None,
+                  "attn_mean_abs": float(err.mean()) if err.size else None,
+                  "bars": {"max_abs": 2e-2, "mean_abs": 5e-3}}
+        if lse_head0 is not None:
+            gl = lse_head0[0, 0].double().numpy()[rows]
+            rr = rl[0, 0][rows]
+            fin = np.isfinite(rr)
+            parity["lse_max_abs"] = float(np.abs(gl[fin] - rr[fin]).max()) if fin.any() else None
+    return parity, {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
@@ -639,7 +665,15 @@ def main(argv=None):
                 f.write(json.dumps(rec) + "\n")
                 print(json.dumps(rec), file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, mask_cpu, args.cpu_sample_blocks)
+        # the timed call's output for head 0, with its LSE from one more call on the same lists
+        o2, lse = sa.fwd_lists(q, k, v, sel["kept_idx"], sel["kept_cnt"], w.bq, w.bk, return_lse=True,
+                               row_order=order)
+        torch.cuda.synchronize()
+        same_o = bool(torch.equal(o2, o))
+        parity, result["cpu_baseline"] = cpu_baseline(w, x, mask_cpu, args.cpu_sample_blocks,
+                                                      o[:, :1].float().cpu(), lse[:, :1].float().cpu())
+        parity["lse_call_output_equal"] = same_o
+        result["parity"] = parity
     print(json.dumps(result), flush=True)
     return 0
 
