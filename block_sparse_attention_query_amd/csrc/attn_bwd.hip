@@ -475,21 +475,25 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
       asm volatile("" : "+v"(wp[h][u][2 * g]), "+v"(wp[h][u][2 * g + 1]), "+v"(ws[h][u][2 * g]),
                    "+v"(ws[h][u][2 * g + 1]));
     };
-    // phases A and B: step n = 8 h + s of the S / dP products
+    // phases A and B: step n = 8 h + s of the S / dP products, their Q and dO operands read two
+    // product steps ahead (a ring of three)
     constexpr int SS = D / 16;
-    bf16x8 cur[2], nxt[2];
-    cur[0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[0]);
-    cur[1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[0]);
+    bf16x8 ring[3][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      ring[a][0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[a % SS] + 32 * (a / SS) * C::ROWB);
+      ring[a][1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[a % SS] + 32 * (a / SS) * C::ROWB);
+    }
 #pragma unroll
     for (int n = 0; n < 2 * SS; ++n) {
       const int h = n / SS, s = n % SS;
-      if (n + 1 < 2 * SS) {
-        const int h1 = (n + 1) / SS, s1 = (n + 1) % SS;
-        nxt[0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s1] + 32 * h1 * C::ROWB);
-        nxt[1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s1] + 32 * h1 * C::ROWB);
+      if (n + 2 < 2 * SS) {
+        const int h1 = (n + 2) / SS, s1 = (n + 2) % SS;
+        ring[(n + 2) % 3][0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(qt + roff[s1] + 32 * h1 * C::ROWB);
+        ring[(n + 2) % 3][1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(gt + roff[s1] + 32 * h1 * C::ROWB);
       }
-      sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[0], kf[s], sc[h], 0, 0, 0);
-      dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[1], vf[s], dp[h], 0, 0, 0);
+      sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % 3][0], kf[s], sc[h], 0, 0, 0);
+      dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % 3][1], vf[s], dp[h], 0, 0, 0);
       if (2 * n < NPART && sbn >= 0) {
         kv_part(cp, wave, lane, doff, 2 * n, KVDma<D>::PW, C::OFF_G, C::OFF_L);
         if (2 * n + 1 < NPART) kv_part(cp, wave, lane, doff, 2 * n + 1, KVDma<D>::PW, C::OFF_G, C::OFF_L);
@@ -500,8 +504,6 @@ __global__ __launch_bounds__(128, 1) void attn_bwd_dkdv_kernel(
         ps_quad(0, qd >> 1, qd & 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
     }
 
     // phases C and D: dV += P^T dO and dK += dS^T Q, item j = (h, u, channel tile c); the
