@@ -245,16 +245,30 @@ __global__ __launch_bounds__(1024) void km_scan_kernel(int32_t* __restrict__ his
 }
 
 // Pass 2b. Grid BH, 1024 threads (thread = label): offsets[c] = the exclusive prefix of the label
-// totals, offsets[C] = N.
-__global__ __launch_bounds__(KM_MAXC) void km_offsets_kernel(int C, int32_t* __restrict__ offsets) {
+// totals, offsets[C] = N; and the order in which the centroid update visits the clusters, largest
+// first (ties to the lower label): ord[bh][r] = the label of rank r, ord[bh][r] = r for the
+// padding ranks C <= r < CP. One workgroup sums one cluster, so the largest clusters set the
+// update's time unless they start first.
+__global__ __launch_bounds__(KM_MAXC) void km_offsets_kernel(int C, int CP, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ ord) {
   __shared__ int scratch[KM_MAXC / 64];
+  __shared__ int sz[KM_MAXC];
   const int bh = blockIdx.x, c = threadIdx.x;
   int32_t* off = offsets + (size_t)bh * (C + 1);
   const int v = c < C ? off[c] : 0;
+  if (c < C) sz[c] = v;
   int total;
   const int ex = block_exclusive_scan<KM_MAXC>(v, scratch, &total);
   if (c < C) off[c] = ex;
   if (c == 0) off[C] = total;
+  __syncthreads();  // sz is complete
+  if (c < C) {
+    int r = 0;
+    for (int j = 0; j < C; ++j) r += (sz[j] > v) | ((sz[j] == v) & (j < c));
+    ord[(size_t)bh * CP + r] = c;
+  } else if (c < CP) {
+    ord[(size_t)bh * CP + c] = c;
+  }
 }
 
 // Pass 3. Grid (BH, ceil(N / 256)): perm[offsets[l] + chunk base[l] + rank] = token.
@@ -276,16 +290,20 @@ __global__ __launch_bounds__(KM_CH) void km_scatter_kernel(const int32_t* __rest
 // 16-byte load per row) over the members o0 + r, o0 + r + RS, ... of the cluster's run of the
 // permuted order, eight rows in flight; the RS partial sums of a channel are added in the order
 // of r, so the result is deterministic.
+// Workgroup (bh, r) takes cluster ord[bh][r], so that the grid's first round holds the largest
+// clusters of every head.
 template <int D>
 __global__ __launch_bounds__(256) void km_update_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                        const int32_t* __restrict__ offsets, int N, int C, int CP,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ ord, int N, int C, int CP,
                                                         float* __restrict__ cen, __bf16* __restrict__ chi,
                                                         __bf16* __restrict__ clo, float* __restrict__ cn) {
   constexpr int LPR = D / 8;    // lanes per row: 16 bytes (8 channels) each
   constexpr int RS = 256 / LPR;  // row slots: members o0 + r, o0 + r + RS, ... go to slot r
   __shared__ double part[RS][D];
   __shared__ float red[4];
-  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int c = min(max(ord[(size_t)bh * CP + blockIdx.y], 0), CP - 1);
   const int r = tid / LPR, cs = tid % LPR;
   int o0 = 0, o1 = 0;
   if (c < C) {
@@ -900,7 +918,7 @@ int pad32(int c) { return (c + 31) / 32 * 32; }
 size_t kmeans_workspace_bytes(int BH, int N, int d, int C) {
   const size_t CP = (size_t)pad32(C), nch = (size_t)(N + KM_CH - 1) / KM_CH;
   return 2 * al256((size_t)BH * CP * d * 2) + al256((size_t)BH * CP * 4) + al256((size_t)BH * N * 4) +
-         al256((size_t)BH * nch * C * 4);
+         al256((size_t)BH * nch * C * 4) + al256((size_t)BH * CP * 4);
 }
 
 hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, const float* init, float* cen,
@@ -916,6 +934,8 @@ hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, 
   int32_t* rank = reinterpret_cast<int32_t*>(p);
   p += al256((size_t)BH * N * 4);
   int32_t* hist = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)BH * nch * C * 4);
+  int32_t* ord = reinterpret_cast<int32_t*>(p);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   hipError_t e;
 #define SA_KM(D_)                                                                                                  \
@@ -929,11 +949,11 @@ hipError_t launch_kmeans(const void* x, int BH, int N, int d, int C, int iters, 
                        rank, hist);                                                                                \
     hipLaunchKernelGGL(km_scan_kernel, dim3((unsigned)BH, (unsigned)((C + 15) / 16)), dim3(1024), 0, stream, hist, C, \
                        nch, offsets);                                                                              \
-    hipLaunchKernelGGL(km_offsets_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, C, offsets);              \
+    hipLaunchKernelGGL(km_offsets_kernel, dim3((unsigned)BH), dim3(KM_MAXC), 0, stream, C, CP, offsets, ord);     \
     hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)BH, (unsigned)nch), dim3(KM_CH), 0, stream, labels, rank,  \
                        hist, offsets, N, C, nch, perm);                                                            \
     hipLaunchKernelGGL((km_update_kernel<D_>), dim3((unsigned)BH, (unsigned)CP), dim3(256), 0, stream, xs, perm,     \
-                       offsets, N, C, CP, cen, chi, clo, cn);                                                      \
+                       offsets, ord, N, C, CP, cen, chi, clo, cn);                                                 \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                                           \
   }
   if (d == 128) {

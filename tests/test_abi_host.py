@@ -414,7 +414,7 @@ def test_cluster_workspace_sizes():
     bh, n, d, c = 2, 1000, 64, 40
     cp, nch = 64, 4
     assert lib.sparse_attn_kmeans_workspace_size(1, 2, n, d, c) == \
-        2 * al(bh * cp * d * 2) + al(bh * cp * 4) + al(bh * n * 4) + al(bh * nch * c * 4)
+        2 * al(bh * cp * d * 2) + al(bh * cp * 4) + al(bh * n * 4) + al(bh * nch * c * 4) + al(bh * cp * 4)
     mt = 8 + 8
     assert lib.sparse_attn_cluster_fwd_workspace_size(1, 2, n, 8, 40, 128) == \
         al(bh * mt * 16) + al(bh * 4) + al(bh * 8 * 40 * 4) + al(bh * 8 * 4)
