@@ -592,6 +592,17 @@ def main(argv=None):
     flops = executed_flops(mask_cpu, N, w.bq, w.bk, d)
     tile_flops = 4.0 * d * w.bq * w.bk * float(mask_cpu.sum())  # what the kernel runs, padding included
     density = float(mask_cpu.mean())
+    # what the hybrid rule kept: Top-k alone keeps k blocks per row, so rows above k are the ones
+    # whose Top-p prefix was longer (per group of 8 heads)
+    k_blocks = sa.topk_count(w.k_frac, mask_cpu.shape[-1])
+    cnt = mask_cpu.sum(-1, dtype=np.int64).reshape(B, H, -1)
+    groups = [(h0, min(H, h0 + 8)) for h0 in range(0, H, 8)]
+    selection = {"topk_blocks": k_blocks, "kept_per_row_mean": round(float(cnt.mean()), 2),
+                 "kept_per_row_max": int(cnt.max()),
+                 "rows_topp_longer": round(float((cnt > k_blocks).mean()), 4),
+                 "by_head_group": [{"heads": f"{a}-{b - 1}", "kept_per_row_mean": round(float(cnt[:, a:b].mean()), 2),
+                                    "rows_topp_longer": round(float((cnt[:, a:b] > k_blocks).mean()), 4)}
+                                   for a, b in groups]}
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -642,6 +653,7 @@ def main(argv=None):
                      "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_bytes": alg_bytes, "l2_hit_rate": l2_hit},
         "pool_gbs": round(2 * B * H * N * d * q.element_size() / (pool_ms * 1e-3) / 1e9, 1),
+        "selection": selection,
         "input_generation_s": round(gen_s, 1),
     }
     if args.sweep_out:
