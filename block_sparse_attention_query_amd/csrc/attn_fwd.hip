@@ -25,6 +25,8 @@
 
 namespace sa {
 
+constexpr int kPairMaxKB = 4096;  // key blocks per head of the paired 64-query walk
+
 // ---------------------------------------------------------------- mask -> kept-block lists
 
 // One wave per mask row: ascending kept indices and their count.
@@ -239,12 +241,21 @@ __device__ __forceinline__ void copy_tile(const char* __restrict__ base, int kb,
 // windows form runs of wt_nw rows, so win = wt_nw gives the SQuad global pass. A query block
 // visits the contiguous range of key blocks that covers its rows' windows, and keys outside a
 // query's window get score -inf element by element.
-template <int D, int BQ, bool WT = false, bool WIN = false>
+//
+// PAIR (BQ = 128): the rows are those of 64-query blocks, taken two at a time. Workgroup (b, h, q)
+// computes 64-query rows 2 q (waves 0, 1) and 2 q + 1 (waves 2, 3) of the nqb64 rows per head, and
+// walks the union of their kept lists (at most kPairMaxKB key blocks per row), every union entry
+// carrying whether each row keeps it. A wave scores a block its row does not keep at -inf, which
+// adds exactly nothing to its softmax, so each row's result is bit-identical to that of the
+// one-row walk over its own list, while one 4-wave workgroup of 64 KiB of LDS serves 128 queries
+// (two per CU, two waves per SIMD) instead of a 2-wave workgroup serving 64 (one wave per SIMD).
+template <int D, int BQ, bool WT = false, bool WIN = false, bool PAIR = false>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ kidx, const int32_t* __restrict__ kcnt, int N, int nqb, int nkb, float c_log2,
     void* __restrict__ o, float* __restrict__ lse, int wt_nw, int wt_w, int win,
-    const int32_t* __restrict__ row_order) {
+    const int32_t* __restrict__ row_order, int nqb64 = 0) {
+  static_assert(!PAIR || (BQ == 128 && !WT && !WIN), "the paired walk runs two 64-query rows per 4-wave workgroup");
   using C = DCfg<D, BQ>;
   __shared__ __attribute__((aligned(1024))) char kbuf_[2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf_[2 * C::TILE];
@@ -264,20 +275,77 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   const int hf = lane >> 5;
   int cnt, kb_first = 0;
   const int32_t* list = kidx + (size_t)tile * nkb;
+  // PAIR: the union list in LDS, entries kb | (row 2q keeps it) << 14 | (row 2q + 1 keeps it) << 15
+  const __attribute__((address_space(3))) uint16_t* ulist = nullptr;
+  const int half = wave >> 1;  // PAIR: the row of this wave within the pair
+  int pair_cnt = 0;
+  if constexpr (PAIR) {
+    __shared__ uint32_t pmask[2][kPairMaxKB / 32];
+    __shared__ uint16_t ul_[kPairMaxKB];
+    __shared__ int ucnt;
+    const int nw = (nkb + 31) >> 5;
+    const int rA = 2 * qb, rB = 2 * qb + 1;
+    const int32_t* la = kidx + ((size_t)bh * nqb64 + rA) * nkb;
+    const int32_t* lb = kidx + ((size_t)bh * nqb64 + rB) * nkb;
+    const int ca = min(max(kcnt[(size_t)bh * nqb64 + rA], 0), nkb);
+    const int cb = rB < nqb64 ? min(max(kcnt[(size_t)bh * nqb64 + rB], 0), nkb) : 0;
+    for (int i = threadIdx.x; i < 2 * nw; i += BQ * 2) pmask[i / nw][i % nw] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ca; i += BQ * 2) {
+      const int e = min(max(la[i], 0), nkb - 1);
+      atomicOr(&pmask[0][e >> 5], 1u << (e & 31));
+    }
+    for (int i = threadIdx.x; i < cb; i += BQ * 2) {
+      const int e = min(max(lb[i], 0), nkb - 1);
+      atomicOr(&pmask[1][e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int run = 0;
+      for (int w0 = 0; w0 < nw; w0 += 64) {
+        const int w = w0 + lane;
+        const uint32_t a = w < nw ? pmask[0][w] : 0u, b = w < nw ? pmask[1][w] : 0u;
+        uint32_t u = a | b;
+        const int c = __popc(u);
+        int pre = c;  // inclusive prefix over the lanes
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const int t = __shfl_up(pre, m, 64);
+          if (lane >= m) pre += t;
+        }
+        int pos = run + pre - c;
+        while (u) {
+          const int bit = __ffs(u) - 1;
+          u &= u - 1u;
+          ul_[pos++] = (uint16_t)((w * 32 + bit) | (((a >> bit) & 1u) << 14) | (((b >> bit) & 1u) << 15));
+        }
+        run += __shfl(pre, 63, 64);
+      }
+      if (lane == 0) ucnt = run;
+    }
+    __syncthreads();
+    ulist = (const __attribute__((address_space(3))) uint16_t*)ul_;
+    pair_cnt = __builtin_amdgcn_readfirstlane(ucnt);
+  }
   if constexpr (WIN) {
     // key blocks from the start of the first row's window to the end of the last row's window
     const int r0 = qb * BQ, r1 = min(N, r0 + BQ) - 1;
     const int wend = min(N, (r1 / win + 1) * win);
     kb_first = (r0 / win) * win / BK;
     cnt = (wend - 1) / BK - kb_first + 1;
+  } else if constexpr (PAIR) {
+    cnt = pair_cnt;
   } else {
     cnt = min(max(kcnt[tile], 0), nkb);
   }
   // list entries are clamped to [0, nKB) so that no load leaves K or V
   auto blk = [&](int i) {
     if constexpr (WIN) return kb_first + i;
+    else if constexpr (PAIR) return (int)(ulist[i] & 0x0fffu);
     else return min(max(list[i], 0), nkb - 1);
   };
+  // PAIR: whether this wave's row keeps union entry e (an entry as stored, or -1 past the end)
+  auto keeps = [&](int e) { return e >= 0 && ((e >> (14 + half)) & 1) != 0; };
 
   const size_t head_off = (size_t)bh * N * D * 2;
   const char* qbase = static_cast<const char*>(q) + head_off;
@@ -339,7 +407,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   // running max in the scaled log2 domain, shared by the lane pair. With WIN a query can meet
   // blocks whose keys all lie outside its window; a finite start keeps exp2(-inf - m) at 0 there
   // (exp2(-inf + inf) would be undefined), and the first block with a key raises it as before.
-  float m_run = WIN ? -3.0e38f : -INFINITY;
+  float m_run = (WIN || PAIR) ? -3.0e38f : -INFINITY;
   float l_run = 0.f;  // this lane's part of the running sum
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -378,6 +446,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       const int key = kb * BK + 8 * (i >> 2) + 4 * hf + (i & 3);
       if (key >= N) sc[0][i] = -INFINITY;
       if (key + 32 >= N) sc[1][i] = -INFINITY;
+    }
+  };
+  // PAIR: a block this wave's row does not keep: every score -inf
+  auto mask_all = [&](f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = -INFINITY, b = -INFINITY;
+      // the empty asm keeps this a branch: as selects hoisted out of it the mask would cost
+      // every block
+      asm volatile("" : "+v"(a), "+v"(b));
+      sc[0][i] = a;
+      sc[1][i] = b;
     }
   };
   // WIN: keys outside this lane's window (and past N) get score -inf
@@ -507,7 +587,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
   // kept-list entries t + 1 and t + 2 of step t, in scalar registers; entry t + 3 is fetched
   // during step t by a vector load (counted by vmcnt, which the next step's barrier drains), so
   // that no scalar load waits right behind the barrier
-  int e1 = cnt > 1 ? blk(1) : -1, e2 = cnt > 2 ? blk(2) : -1;
+  int e1, e2;
+  if constexpr (PAIR) {
+    e1 = cnt > 1 ? (int)ulist[1] : -1;
+    e2 = cnt > 2 ? (int)ulist[2] : -1;
+  } else {
+    e1 = cnt > 1 ? blk(1) : -1;
+    e2 = cnt > 2 ? blk(2) : -1;
+  }
   int vl = 0, lz = 0;
   asm volatile("" : "+v"(lz));  // a zero opaque to the compiler, which makes the list load a vector load
   auto step = [&](int t, const f32x16 (&sc)[2], f32x16 (&sn)[2], const lchar* kn, lchar* vc, lchar* kf, lchar* vf,
@@ -518,9 +605,20 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     // the DMA for K(t+2) and V(t+1) is issued between the score MFMAs, so that the waves released
     // by the barrier start on the matrix cores instead of queueing their copies first
     int blk1, blk2;
+    bool keep1 = true;  // PAIR: this wave's row keeps block t + 1
     if constexpr (WIN) {
       blk2 = t + 2 < cnt ? blk(t + 2) : -1;
       blk1 = t + 1 < cnt ? blk(t + 1) : -1;
+    } else if constexpr (PAIR) {
+      // union entries (with their row bits) t + 1, t + 2 in scalar registers, t + 3 read from LDS
+      if (t > 0) {
+        e1 = e2;
+        e2 = t + 2 < cnt ? __builtin_amdgcn_readfirstlane(vl) : -1;
+      }
+      if (t + 3 < cnt) vl = ulist[t + 3];
+      blk1 = e1 >= 0 ? (e1 & 0x0fff) : -1;
+      blk2 = e2 >= 0 ? (e2 & 0x0fff) : -1;
+      keep1 = keeps(e1);
     } else {
       if (t > 0) {
         e1 = e2;
@@ -547,6 +645,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
       scores_p(kn, sn, sc, pw, rs, issue);
       if constexpr (NEXT == 2) mask_tail(sn, blk1);
       if constexpr (WIN) mask_win(sn, blk1);
+      if constexpr (PAIR) {
+        if (!keep1) mask_all(sn);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) p_word(sc, j, pw, rs);
@@ -574,6 +675,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_fwd_kernel(
     scores(kb0, sa);
     if (ragged_last && cnt == 1) mask_tail(sa, blk(0));
     if constexpr (WIN) mask_win(sa, blk(0));
+    if constexpr (PAIR) {
+      if (!keeps((int)ulist[0])) mask_all(sa);
+    }
     raise_max(block_max(sa));
     // steps whose next block is a full one, unrolled by two so that S alternates between sa
     // and sb and the buffers between their even / odd roles without copies
@@ -681,6 +785,16 @@ static hipError_t launch_attn_t(const void* q, const void* k, const void* v, con
                                 const int32_t* kcnt, int BH, int N, int nqb, int nkb, float c_log2, void* o,
                                 float* lse, const int32_t* row_order, hipStream_t stream) {
   if constexpr (DT == kBF16) {
+    if constexpr (BQ == 64) {
+      // pairs of 64-query rows on the 4-wave kernel (the rows' order does not apply)
+      if (nkb <= kPairMaxKB) {
+        const int nqb128 = (N + 127) / 128;
+        hipLaunchKernelGGL((attn_fwd_kernel<D, 128, false, false, true>), dim3((unsigned)(BH * nqb128)),
+                           dim3(DCfg<D, 128>::NT), 0, stream, q, k, v, kidx, kcnt, N, nqb128, nkb, c_log2, o, lse, 0,
+                           0, 0, nullptr, nqb);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<D, BQ>), dim3((unsigned)(BH * nqb)), dim3(DCfg<D, BQ>::NT), 0, stream,
                        q, k, v, kidx, kcnt, N, nqb, nkb, c_log2, o, lse, 0, 0, 0, row_order);
   } else {
