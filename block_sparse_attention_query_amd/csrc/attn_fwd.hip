@@ -785,8 +785,10 @@ static hipError_t launch_attn_t(const void* q, const void* k, const void* v, con
                                 const int32_t* kcnt, int BH, int N, int nqb, int nkb, float c_log2, void* o,
                                 float* lse, const int32_t* row_order, hipStream_t stream) {
   if constexpr (DT == kBF16) {
-    if constexpr (BQ == 64) {
-      // pairs of 64-query rows on the 4-wave kernel (the rows' order does not apply)
+    if constexpr (BQ == 64 && D == 128) {
+      // pairs of 64-query rows on the 4-wave kernel (the rows' order does not apply). With d = 64
+      // the one-row kernel's 32 KiB of LDS already lets five 2-wave workgroups share a CU, and
+      // the union's extra blocks then cost more than the pairing gains.
       if (nkb <= kPairMaxKB) {
         const int nqb128 = (N + 127) / 128;
         hipLaunchKernelGGL((attn_fwd_kernel<D, 128, false, false, true>), dim3((unsigned)(BH * nqb128)),

@@ -119,8 +119,9 @@ size_t sparse_attn_fwd_workspace_size(int B, int H, int N, int Bq, int Bk);
  *               aligned; overwritten.
  * The mask is compacted into ascending kept-block lists in the workspace, then one workgroup
  * per (b, h, query block) walks its list with bf16 (or, for SA_F32, fp32) MFMA and an fp32
- * online softmax (for SA_BF16 with Bq = 64, one workgroup per two neighbouring query blocks walks
- * the union of their lists, each block scored only for the rows that keep it; same results).
+ * online softmax (for SA_BF16 with d = 128 and Bq = 64, one workgroup per two neighbouring query
+ * blocks walks the union of their lists, each block scored only for the rows that keep it; same
+ * results).
  */
 int sparse_attn_fwd(const void* q, const void* k, const void* v, int dtype, const uint8_t* mask,
                     int B, int H, int N, int d, int Bq, int Bk, double scale, void* o, float* lse,
@@ -174,7 +175,7 @@ int sparse_attn_row_order(const int32_t* kept_cnt, int B, int H, int nqb, int32_
  * sparse_attn_fwd_lists with workgroup w computing row row_order[w] (from sparse_attn_row_order;
  * entries are clamped to the row range, and an order that is not a permutation leaves rows
  * uncomputed or computed twice). Results equal those of sparse_attn_fwd_lists bit for bit.
- * With SA_BF16 and Bq = 64 (up to 4096 key blocks per head) the rows run in pairs of
+ * With SA_BF16, d = 128 and Bq = 64 (up to 4096 key blocks per head) the rows run in pairs of
  * neighbouring 64-query blocks and row_order is not used.
  */
 int sparse_attn_fwd_lists_ordered(const void* q, const void* k, const void* v, int dtype, const int32_t* kept_idx,
