@@ -1,5 +1,6 @@
-"""GPU checks of the forward on 64-query blocks, which runs them two at a time on the 4-wave kernel
-over the union of the pair's kept lists (through the C ABI).
+"""GPU checks of the forward on 64-query blocks, which for d = 128 runs them two at a time on the
+4-wave kernel over the union of the pair's kept lists (through the C ABI; d = 64 keeps the one-row
+kernel, for which the same properties hold trivially).
 
 A row's result must not depend on its partner's list: each wave scores the blocks its own row does
 not keep at -inf, which adds exactly nothing. So changing only the partner rows' lists must leave
@@ -126,7 +127,7 @@ def test_all_partner_rows_empty():
 
 def test_above_union_limit_runs_one_row_kernel():
     """4097 key blocks: above the paired walk's limit, the one-row kernel serves 64-query blocks."""
-    B, H, d = 1, 1, 64
+    B, H, d = 1, 1, 128
     N = 4097 * 64 - 13
     q, k, v = (t.to(DEV) for t in rand_qkv(B, H, N, d, 12, qk_scale=1.0))
     nqb = nkb = -(-N // 64)
