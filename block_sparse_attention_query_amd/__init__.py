@@ -18,7 +18,9 @@ import torch
 
 from . import _lib
 from ._lib import (SA_BF16, SA_F32, SA_PAT_DIAG, SA_PAT_GLOBAL, SA_PAT_LOCAL, SA_PAT_MULTIDIAG,  # noqa: F401
-                   SA_PAT_STRIPE, SparseAttnError)
+                   SA_PAT_STRIPE, SA_SELECT_FUSED_NKB, SparseAttnError)
+
+SELECT_FUSED_NKB = SA_SELECT_FUSED_NKB
 
 __all__ = ["pool_qk", "select_mask", "fwd", "fwd_noalloc", "fwd_lists", "row_order", "fwd_workspace_size", "bwd", "bwd_workspace_size",
            "pattern_mask",
@@ -82,10 +84,11 @@ def pool_qk(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, out=None):
 
 
 def select_mask(q_pool: torch.Tensor, k_pool: torch.Tensor, k_frac: float, p: float, scale: float | None = None,
-                kept_lists: bool = False, out: dict | None = None):
+                kept_lists: bool = False, out: dict | None = None, probs: bool = True):
     """Pooled probabilities and the hybrid Top-k U Top-p block mask.
 
-    Returns a dict with ``probs`` (float64 ``[B,H,nQB,nKB]``), ``mask`` (uint8) and, when
+    Returns a dict with ``probs`` (float64 ``[B,H,nQB,nKB]``, left out when ``probs`` is False,
+    which rows of at most SA_SELECT_FUSED_NKB key blocks allow), ``mask`` (uint8) and, when
     ``kept_lists`` is set, ``kept_idx`` / ``kept_cnt`` (int32). ``out`` may pass a dict of
     preallocated buffers under the same keys.
     """
@@ -98,19 +101,22 @@ def select_mask(q_pool: torch.Tensor, k_pool: torch.Tensor, k_frac: float, p: fl
         raise ValueError("q_pool and k_pool shapes disagree")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q_pool.device
-    want = {"probs": ((B, H, nqb, nkb), torch.float64), "mask": ((B, H, nqb, nkb), torch.uint8)}
+    want = {"mask": ((B, H, nqb, nkb), torch.uint8)}
+    if probs:
+        want["probs"] = ((B, H, nqb, nkb), torch.float64)
     if kept_lists:
         want["kept_idx"] = ((B, H, nqb, nkb), torch.int32)
         want["kept_cnt"] = ((B, H, nqb), torch.int32)
     given = out or {}
     out = {name: (_check_out(given[name], shp, dt, dev) if name in given else torch.empty(shp, dtype=dt, device=dev))
            for name, (shp, dt) in want.items()}
-    probs, mask = out["probs"], out["mask"]
+    probs_ptr = out["probs"].data_ptr() if probs else None
+    mask = out["mask"]
     idx_ptr = cnt_ptr = None
     if kept_lists:
         idx_ptr, cnt_ptr = out["kept_idx"].data_ptr(), out["kept_cnt"].data_ptr()
     _lib.check(_lib.lib().sparse_attn_select_mask(q_pool.data_ptr(), k_pool.data_ptr(), B, H, nqb, nkb, d, scale,
-                                                  float(k_frac), float(p), probs.data_ptr(), mask.data_ptr(),
+                                                  float(k_frac), float(p), probs_ptr, mask.data_ptr(),
                                                   idx_ptr, cnt_ptr, _stream(q_pool)))
     return out
 

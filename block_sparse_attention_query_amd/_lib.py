@@ -16,6 +16,7 @@ SA_ERR_HIP = -3
 SA_BF16 = 0
 SA_F32 = 1
 SA_PAT_LOCAL, SA_PAT_GLOBAL, SA_PAT_DIAG, SA_PAT_MULTIDIAG, SA_PAT_STRIPE = 1, 2, 4, 8, 16
+SA_SELECT_FUSED_NKB = 1280  # longest rows whose selection may leave out the probabilities
 SA_SQUAD_LOCAL, SA_SQUAD_GLOBAL = 0, 1
 SA_NOALLOC_SCRATCH_BYTES = 32 << 20
 

@@ -141,13 +141,16 @@ int sparse_attn_pool_qk(const void* q, const void* k, int dtype, int B, int H, i
 int sparse_attn_select_mask(const double* q_pool, const double* k_pool, int B, int H, int nqb, int nkb, int d,
                             double scale, double k_frac, double p, double* probs, uint8_t* mask, int32_t* kept_idx,
                             int32_t* kept_cnt, void* stream) {
-  if (!q_pool || !k_pool || !probs || !mask) return fail(SA_ERR_INVALID_ARG, "select_mask: null pointer");
+  if (!q_pool || !k_pool || !mask) return fail(SA_ERR_INVALID_ARG, "select_mask: null pointer");
   if ((kept_idx == nullptr) != (kept_cnt == nullptr))
     return fail(SA_ERR_INVALID_ARG, "select_mask: kept_idx and kept_cnt must both be given or both be NULL");
   if (nqb <= 0 || nkb <= 0) return fail(SA_ERR_INVALID_ARG, "select_mask: nqb and nkb must be positive");
   int rc = check_shape(B, H, 1, d);
   if (rc) return rc;
   if (nkb > SA_MAX_NKB) return fail(SA_ERR_UNSUPPORTED, "select_mask: nkb=%d exceeds %d", nkb, SA_MAX_NKB);
+  if (!probs && nkb > SA_SELECT_FUSED_NKB)
+    return fail(SA_ERR_INVALID_ARG, "select_mask: probs may be NULL only for nkb <= %d (nkb=%d)",
+                SA_SELECT_FUSED_NKB, nkb);
   if ((long long)B * H * nqb > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "select_mask: too many rows");
   if ((cdiv(nqb, 64)) > 65535) return fail(SA_ERR_UNSUPPORTED, "select_mask: nqb too large");
   if (!(scale > 0.0) || !isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "select_mask: scale must be finite and > 0");

@@ -13,9 +13,10 @@
 // except for rows that sit within rounding of a threshold.
 //
 // Kernel 1 (scores_kernel) is a float64 GEMM per head on the matrix cores, written into `probs`.
-// Kernel 2 (select_kernel) takes one row per workgroup: softmax in place, then orders only the
-// entries that can belong to the kept prefix, a chunked prefix sum for m*, then the mask row and
-// optional lists.
+// Kernel 2 takes the rows: select_rows_kernel one wave per row in registers, select_kernel (rows
+// longer than a wave holds) one workgroup per row; softmax in place, then only the entries that can
+// belong to the kept prefix are ordered, running sums give m*, then the mask row and optional lists.
+// Without `probs`, select_fused_kernel does both: scores of 16 rows in LDS, then the rows' selection.
 #include <algorithm>
 
 #include "sa_common.h"
@@ -435,31 +436,21 @@ __device__ __forceinline__ int64_t bucket_floor(int b) {
   return (e << 52) | ((b & 1) ? (int64_t)0 : ((int64_t)1 << 51));
 }
 
+// Softmax and hybrid selection of one row whose scores one wave holds in registers: v[u] is the
+// score of entry 64 u + lane (-inf past the end of the row). P (NULL: not written) receives the
+// probabilities, mrow the mask row, out / cnt_out (both NULL or neither) the ascending kept list
+// and its length. s_key and s_val are 64 entries each of LDS scratch private to the wave.
 template <int R>
-__global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ probs, uint8_t* __restrict__ mask,
-                                                          int32_t* __restrict__ kept_idx,
-                                                          int32_t* __restrict__ kept_cnt, int rows, int nkb, int k,
-                                                          double p) {
-  __shared__ int64_t s_key[4][64];
-  __shared__ double s_val[4][64];
+__device__ __forceinline__ void select_row(double (&v)[R], int nkb, int k, double p, double* __restrict__ P,
+                                           uint8_t* __restrict__ mrow, int32_t* __restrict__ out,
+                                           int32_t* __restrict__ cnt_out, int64_t* s_key, double* s_val) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const size_t row = (size_t)blockIdx.x * 4 + wave;
-  if (row >= (size_t)rows) return;  // whole wave leaves; nothing below synchronises the workgroup
   const uint64_t below = (1ull << lane) - 1ull;
-  double* P = probs + row * (size_t)nkb;
-
-  // softmax of the row (kernel 1 left the scores in `probs`); P is written back in place
   int64_t key[R];  // key of entry 64 u + lane, -1 past the end of the row
   {
-    double v[R];
     double mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int j = 64 * u + lane;
-      v[u] = j < nkb ? P[j] : -INFINITY;
-      mx = fmax(mx, v[u]);
-    }
+    for (int u = 0; u < R; ++u) mx = fmax(mx, v[u]);
     mx = wave_max_dpp(mx);
     double sum = 0.0;
 #pragma unroll
@@ -476,7 +467,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
       key[u] = -1;
       if (j < nkb) {
         const double pj = v[u] / sum;
-        P[j] = pj;
+        if (P != nullptr) P[j] = pj;
         key[u] = __double_as_longlong(pj);
       }
     }
@@ -550,12 +541,12 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
       for (int u = 0; u < R; ++u) {
         const bool in = key[u] >= lo && key[u] <= hi;
         const uint64_t bal = __ballot(in);
-        if (in) s_key[wave][base + __popcll(bal & below)] = key[u];
+        if (in) s_key[base + __popcll(bal & below)] = key[u];
         base += __popcll(bal);
       }
       wave_sync();
       const bool mine = lane < nb;
-      const int64_t kc = mine ? s_key[wave][lane] : -1;
+      const int64_t kc = mine ? s_key[lane] : -1;
       int rank = 0;
       for (int x = 0; x < nb; ++x) {
         const uint32_t xl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)kc, x);
@@ -565,9 +556,9 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
       }
       int n_p = 0;
       if (p > 0.0 && m_hi < p) {
-        if (mine) s_val[wave][rank] = __longlong_as_double(kc);
+        if (mine) s_val[rank] = __longlong_as_double(kc);
         wave_sync();
-        double run = mine ? s_val[wave][lane] : 0.0;
+        double run = mine ? s_val[lane] : 0.0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const double up = __shfl_up(run, o, 64);
@@ -587,8 +578,6 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
     }
   }
 
-  uint8_t* mrow = mask + row * (size_t)nkb;
-  int32_t* out = kept_idx != nullptr ? kept_idx + row * (size_t)nkb : nullptr;
   int pos0 = 0, n_out = 0;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
@@ -607,7 +596,161 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
       n_out += __popcll(kb);
     }
   }
-  if (out != nullptr && lane == 0) kept_cnt[row] = n_out;
+  if (out != nullptr && lane == 0) *cnt_out = n_out;
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ probs, uint8_t* __restrict__ mask,
+                                                          int32_t* __restrict__ kept_idx,
+                                                          int32_t* __restrict__ kept_cnt, int rows, int nkb, int k,
+                                                          double p) {
+  __shared__ int64_t s_key[4][64];
+  __shared__ double s_val[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  if (row >= (size_t)rows) return;  // whole wave leaves; nothing below synchronises the workgroup
+  // kernel 1 left the scores in `probs`; the probabilities are written back in place
+  double* P = probs + row * (size_t)nkb;
+  double v[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int j = 64 * u + lane;
+    v[u] = j < nkb ? P[j] : -INFINITY;
+  }
+  select_row<R>(v, nkb, k, p, P, mask + row * (size_t)nkb, kept_idx ? kept_idx + row * (size_t)nkb : nullptr,
+                kept_idx ? kept_cnt + row : nullptr, s_key[wave], s_val[wave]);
+}
+
+// ---------------------------------------------------------------- fused scores + selection
+
+// For callers that do not want the probabilities. One workgroup per group of FQ query-block rows
+// of a head: the scores of the whole group stay in LDS, so they never make a round trip through
+// HBM. Phase 1: the group's FQ x nkb scores on the
+// float64 matrix cores, one 16-column tile per wave at a time; the wave keeps the group's Qbar
+// rows as A operands in registers and reads each tile's Kbar rows as B operands straight from
+// memory (one head's Kbar stays in the XCD's L2), the next tile's loads in flight during the
+// current tile's products. Lane (m, kq) of the v_mfma_f64_16x16x4f64 supplies row / column m at
+// channels KS kq .. KS kq + KS - 1 over the KS = D / 4 steps, so each lane reads one contiguous run
+// of its row; the even and odd steps accumulate in two chains that are added at the end. Phase 2:
+// each wave takes rows of the group and runs the per-row softmax and selection on its scores,
+// read from LDS. Workgroups take the (head, group) items in one contiguous range per XCD.
+constexpr int FQ = 16;            // query-block rows per workgroup (the M of the fp64 product)
+constexpr int FW = 8;             // waves per workgroup
+constexpr int FUSED_NKB = 1280;   // FQ rows of float64 scores fill the 160 KiB of LDS
+
+inline int fused_pitch(int nkb) { return std::max(128, (nkb + 15) / 16 * 16); }
+
+template <int D, int R>
+__global__ __launch_bounds__(FW * 64, 1) void select_fused_kernel(const double* __restrict__ qp,
+                                                                  const double* __restrict__ kp, int n_items,
+                                                                  int nqb, int nkb, int pitch, double scale, int k,
+                                                                  double p, uint8_t* __restrict__ mask,
+                                                                  int32_t* __restrict__ kept_idx,
+                                                                  int32_t* __restrict__ kept_cnt) {
+  constexpr int KS = D / 4;  // product steps
+  extern __shared__ __attribute__((aligned(16))) double s_lds[];  // [FQ][pitch] scores
+  const int ngrp = (nqb + FQ - 1) / FQ;
+  const int item = xcd_remap(blockIdx.x, n_items);
+  const int bh = item / ngrp;
+  const int i0 = (item - bh * ngrp) * FQ;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = lane & 15, kq = lane >> 4;
+  const double* qh = qp + (size_t)bh * nqb * D;
+  const double* kh = kp + (size_t)bh * nkb * D;
+
+  // row r of base (clamped to the n rows there are), channels KS kq .. KS kq + KS - 1. Rows past
+  // the end only feed scores that are never read: query rows past nqb and key columns past nkb.
+  auto load_run = [&](const double* base, int r, int n, double (&x)[KS]) {
+    const f64x2* src = reinterpret_cast<const f64x2*>(base + (size_t)min(r, n - 1) * D + KS * kq);
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      const f64x2 w = src[s];
+      x[2 * s] = w[0];
+      x[2 * s + 1] = w[1];
+    }
+  };
+  double a[KS];
+  load_run(qh, i0 + m, nqb, a);
+
+  // tile t: scores of the group's rows against key blocks 16 t .. 16 t + 15, into LDS
+  auto tile = [&](int t, const double (&b)[KS]) {
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+#pragma unroll
+    for (int s = 0; s < KS; s += 2) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], b[s + 1], acc1, 0, 0, 0);
+    }
+    // result element i: row 4 i + kq, column 16 t + m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_lds[(4 * i + kq) * pitch + 16 * t + m] = scale * (acc0[i] + acc1[i]);
+  };
+  // the wave's tiles t = wave, wave + FW, ...: the next tile's loads (clamped to the last tile, so
+  // that the loop body has no branch) are issued before the current tile's products and moved into
+  // place after them, so the products never wait for the loads in flight.
+  const int ntile = (nkb + 15) / 16;
+  double bc[KS], bn[KS];
+  load_run(kh, 16 * min(wave, ntile - 1) + m, nkb, bc);
+  for (int t = wave; t < ntile; t += FW) {
+    load_run(kh, 16 * min(t + FW, ntile - 1) + m, nkb, bn);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out ahead of the products
+    tile(t, bc);
+    __builtin_amdgcn_sched_barrier(0);  // and the moves, which wait for them, come after
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bc[s] = bn[s];
+  }
+  __syncthreads();
+
+  for (int rr = wave; rr < FQ; rr += FW) {
+    const int row = i0 + rr;
+    if (row >= nqb) break;
+    double* srow = s_lds + (size_t)rr * pitch;
+    double v[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int j = 64 * u + lane;
+      v[u] = j < nkb ? srow[j] : -INFINITY;
+    }
+    // the row's LDS becomes the wave's scratch once every lane has read it
+    wave_sync();
+    const size_t g = (size_t)bh * nqb + row;
+    select_row<R>(v, nkb, k, p, nullptr, mask + g * nkb,
+                  kept_idx ? kept_idx + g * nkb : nullptr, kept_idx ? kept_cnt + g : nullptr,
+                  reinterpret_cast<int64_t*>(srow), srow + 64);
+    wave_sync();
+  }
+}
+
+template <int D, int R>
+hipError_t launch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
+                        uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+  const int pitch = fused_pitch(nkb);
+  const size_t lds = (size_t)FQ * pitch * sizeof(double);
+  const auto fn = reinterpret_cast<const void*>(&select_fused_kernel<D, R>);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int n_items = BH * ((nqb + FQ - 1) / FQ);
+  hipLaunchKernelGGL((select_fused_kernel<D, R>), dim3((unsigned)n_items), dim3(FW * 64), lds, stream, qp, kp,
+                     n_items, nqb, nkb, pitch, scale, k, p, mask, kept_idx, kept_cnt);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
+                          uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+  const int r = (nkb + 63) / 64;
+#define SA_FUSED(RR) return launch_fused<D, RR>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream)
+  if (r <= 1) SA_FUSED(1);
+  if (r <= 2) SA_FUSED(2);
+  if (r <= 4) SA_FUSED(4);
+  if (r <= 8) SA_FUSED(8);
+  if (r <= 12) SA_FUSED(12);
+  if (r <= 16) SA_FUSED(16);
+  SA_FUSED(20);
+#undef SA_FUSED
 }
 
 template <int R>
@@ -631,6 +774,14 @@ size_t select_lds_bytes(int np2) {
 hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, int nkb, int d, double scale,
                          int k, double p, double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt,
                          hipStream_t stream) {
+  // Without probs the scores stay on chip (rows of at most FUSED_NKB entries, which the host
+  // checks ensure). With probs the scores pass through it: the two kernels together are faster
+  // than the fused one, whose row phase has only eight waves per CU to hide its latency.
+  if (probs == nullptr) {
+    if (nkb > FUSED_NKB) return hipErrorInvalidValue;
+    if (d == 128) return dispatch_fused<128>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
+    return dispatch_fused<64>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
+  }
   const int tpc = scores_tiles_per_chunk(BH, nqb, nkb);
   const int ntile = (nkb + SK - 1) / SK;
   const dim3 g1((unsigned)((ntile + tpc - 1) / tpc), (unsigned)((nqb + SQ - 1) / SQ), (unsigned)BH);

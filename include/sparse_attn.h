@@ -59,6 +59,9 @@ extern "C" {
 /* Supported values (others return SA_ERR_UNSUPPORTED): d in {64, 128}; Bq in {64, 128};
  * Bk = 64 for sparse_attn_fwd (pooling accepts Bq, Bk in {64, 128}); nKB <= 8192. */
 #define SA_MAX_NKB 8192
+/* Rows of at most this many key blocks are selected in one kernel that keeps the scores on chip;
+ * only there may sparse_attn_select_mask take probs = NULL. */
+#define SA_SELECT_FUSED_NKB 1280
 #define SA_MAX_CLUSTERS 1024  /* clusters per head for the semantic-aware permutation calls */
 
 /*
@@ -83,8 +86,13 @@ int sparse_attn_pool_qk(const void* q, const void* k, int dtype, int B, int H, i
  *   k_frac           Top-k fraction in [0, 1]; k = min(nkb, ceil(k_frac * nkb - 1e-9)).
  *   p                Top-p mass in [0, 1]; keeps the shortest prefix of the descending order
  *                    whose running sum is >= p (p = 0 keeps none by Top-p).
- *   probs            device out, [B, H, nqb, nkb] float64: softmax over j of
- *                    scale * <q_pool[b,h,i], k_pool[b,h,j]>.
+ *   probs            device out or NULL, [B, H, nqb, nkb] float64: softmax over j of
+ *                    scale * <q_pool[b,h,i], k_pool[b,h,j]>. Given, it also holds the scores
+ *                    between the score and selection kernels. NULL (nothing written) is accepted
+ *                    for nkb <= SA_SELECT_FUSED_NKB: one kernel then keeps the scores of 16
+ *                    query-block rows at a time in LDS (no HBM round trip, but slower than the
+ *                    two kernels at the shapes measured); longer rows without probs return
+ *                    SA_ERR_INVALID_ARG. Masks and lists are the same either way.
  *   mask             device out, [B, H, nqb, nkb] uint8, 1 = keep. Row i keeps the first
  *                    max(k, m*) blocks of the order "descending probability, lower index first
  *                    on equality", m* being the Top-p prefix length.

@@ -107,7 +107,7 @@ def test_pool_rejects(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(qp=None), -1), (dict(mask=None), -1), (dict(probs=None), -1), (dict(idx=P), -1), (dict(cnt=P), -1),
+    (dict(qp=None), -1), (dict(mask=None), -1), (dict(probs=None, nkb=1281), -1), (dict(idx=P), -1), (dict(cnt=P), -1),
     (dict(nkb=0), -1), (dict(d=32), -2), (dict(nkb=8193), -2), (dict(k_frac=-0.01), -1), (dict(k_frac=1.01), -1),
     (dict(p=float("nan")), -1), (dict(p=1.5), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1),
 ])
@@ -420,3 +420,14 @@ def test_cluster_workspace_sizes():
         al(bh * mt * 16) + al(bh * 4) + al(bh * 8 * 40 * 4) + al(bh * 8 * 4)
     assert lib.sparse_attn_kmeans_workspace_size(1, 2, n, 96, c) == 0
     assert lib.sparse_attn_cluster_fwd_workspace_size(1, 2, n, 8, 40, 96) == 0
+
+
+def test_select_fused_limit_matches_header():
+    """The binding's limit for leaving out the probabilities is the header's, and the call names it
+    when a longer row comes without them."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "sparse_attn.h")).read()
+    assert int(re.search(r"#define SA_SELECT_FUSED_NKB (\d+)", hdr).group(1)) == _lib.SA_SELECT_FUSED_NKB
+    assert _select(probs=None, nkb=_lib.SA_SELECT_FUSED_NKB + 1) == -1
+    msg = _lib.lib().sparse_attn_last_error().decode()
+    assert "probs" in msg and str(_lib.SA_SELECT_FUSED_NKB) in msg

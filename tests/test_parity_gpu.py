@@ -72,7 +72,24 @@ def check_select(q, k, qp, kp, bq, bk, k_frac, p, lists=True):
         flat_m, flat_i, flat_c = gm.reshape(-1, gm.shape[-1]), idx.reshape(-1, idx.shape[-1]), cnt.reshape(-1)
         for r in range(flat_m.shape[0]):
             np.testing.assert_array_equal(flat_i[r, :flat_c[r]], np.nonzero(flat_m[r])[0])
+    check_no_probs(qp, kp, k_frac, p, sel, lists)
     return sel, ref_mask, info
+
+
+def check_no_probs(qp, kp, k_frac, p, sel, lists, scale=None):
+    """Without the probabilities output the call gives the same mask and lists bit for bit."""
+    s2 = sa.select_mask(qp, kp, k_frac, p, scale, kept_lists=lists, probs=False)
+    assert "probs" not in s2
+    assert torch.equal(s2["mask"], sel["mask"])
+    if lists:
+        assert torch.equal(s2["kept_cnt"], sel["kept_cnt"])
+        m = sel["mask"].reshape(-1, sel["mask"].shape[-1])
+        i1 = sel["kept_idx"].reshape(m.shape)
+        i2 = s2["kept_idx"].reshape(m.shape)
+        c = sel["kept_cnt"].reshape(-1)
+        cols = torch.arange(m.shape[-1], device=m.device)[None, :]
+        used = cols < c[:, None]  # entries past each row's count are unwritten
+        assert torch.equal(torch.where(used, i1, 0), torch.where(used, i2, 0))
 
 
 def fp32_bounds(q, k, v, n_keys):
@@ -266,7 +283,8 @@ def test_lists_out_of_range_entries_are_clamped(dt):
     assert torch.equal(o[0, 1, 3 * bq:4 * bq], torch.zeros_like(o[0, 1, 3 * bq:4 * bq]))  # count -4 -> empty row
 
 
-@pytest.mark.parametrize("nkb,k_frac,p", [(2048, 0.03, 0.9), (2049, 0.03, 0.9), (3000, 0.1, 0.5),
+@pytest.mark.parametrize("nkb,k_frac,p", [(1280, 0.03, 0.9), (1281, 0.03, 0.9), (2048, 0.03, 0.9),
+                                          (2049, 0.03, 0.9), (3000, 0.1, 0.5),
                                           (8192, 0.01, 0.95)])
 def test_select_long_rows(nkb, k_frac, p):
     """Rows of 2048 key blocks (the last size taken by one wave per row) and of 2049-8192 (one
@@ -296,3 +314,8 @@ def test_select_long_rows(nkb, k_frac, p):
     np.testing.assert_array_equal(cnt, flat.sum(-1))
     for r in range(flat.shape[0]):
         np.testing.assert_array_equal(idx[r, :cnt[r]], np.nonzero(flat[r])[0])
+    if nkb <= sa.SELECT_FUSED_NKB:
+        check_no_probs(qp, kp, k_frac, p, sel, True, scale)
+    else:
+        with pytest.raises(sa.SparseAttnError):
+            sa.select_mask(qp, kp, k_frac, p, scale, kept_lists=True, probs=False)
