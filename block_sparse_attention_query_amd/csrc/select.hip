@@ -626,17 +626,19 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
 
 // For callers that do not want the probabilities. One workgroup per group of FQ query-block rows
 // of a head: the scores of the whole group stay in LDS, so they never make a round trip through
-// HBM. Phase 1: the group's FQ x nkb scores on the
-// float64 matrix cores, one 16-column tile per wave at a time; the wave keeps the group's Qbar
-// rows as A operands in registers and reads each tile's Kbar rows as B operands straight from
-// memory (one head's Kbar stays in the XCD's L2), the next tile's loads in flight during the
+// HBM. 16 waves, so that the row phase has a wave per row. Phase 1: the group's FQ x nkb scores on the float64 matrix cores. Waves w and w + 8
+// compute the same 16-column tiles t = w mod 8, + 8, ..., over the first and the second half of
+// the channels, and add their partial scores into the zeroed LDS rows (two float64 adds onto
+// zero, so the sum does not depend on their order). Each wave keeps its half of the group's Qbar
+// rows as A operands in registers and reads each tile's Kbar half-rows as B operands straight
+// from memory (one head's Kbar stays in the XCD's L2), the next tile's loads in flight during the
 // current tile's products. Lane (m, kq) of the v_mfma_f64_16x16x4f64 supplies row / column m at
-// channels KS kq .. KS kq + KS - 1 over the KS = D / 4 steps, so each lane reads one contiguous run
-// of its row; the even and odd steps accumulate in two chains that are added at the end. Phase 2:
-// each wave takes rows of the group and runs the per-row softmax and selection on its scores,
-// read from LDS. Workgroups take the (head, group) items in one contiguous range per XCD.
+// channels h D / 2 + KH kq .. + KH - 1 over the KH = D / 8 steps of half h, so each lane reads
+// one contiguous run; even and odd steps accumulate in two chains. Phase 2: wave r takes row r
+// of the group and runs the per-row softmax and selection on its scores, read from LDS.
+// Workgroups take the (head, group) items in one contiguous range per XCD.
 constexpr int FQ = 16;            // query-block rows per workgroup (the M of the fp64 product)
-constexpr int FW = 8;             // waves per workgroup
+constexpr int FW = 16;            // waves per workgroup: one per row in the row phase
 constexpr int FUSED_NKB = 1280;   // FQ rows of float64 scores fill the 160 KiB of LDS
 
 inline int fused_pitch(int nkb) { return std::max(128, (nkb + 15) / 16 * 16); }
@@ -645,10 +647,11 @@ template <int D, int R>
 __global__ __launch_bounds__(FW * 64, 1) void select_fused_kernel(const double* __restrict__ qp,
                                                                   const double* __restrict__ kp, int n_items,
                                                                   int nqb, int nkb, int pitch, double scale, int k,
-                                                                  double p, uint8_t* __restrict__ mask,
+                                                                  double p, double* __restrict__ probs,
+                                                                  uint8_t* __restrict__ mask,
                                                                   int32_t* __restrict__ kept_idx,
                                                                   int32_t* __restrict__ kept_cnt) {
-  constexpr int KS = D / 4;  // product steps
+  constexpr int KH = D / 8;  // product steps per channel half
   extern __shared__ __attribute__((aligned(16))) double s_lds[];  // [FQ][pitch] scores
   const int ngrp = (nqb + FQ - 1) / FQ;
   const int item = xcd_remap(blockIdx.x, n_items);
@@ -657,74 +660,79 @@ __global__ __launch_bounds__(FW * 64, 1) void select_fused_kernel(const double* 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15, kq = lane >> 4;
+  const int pw = wave & 7;                  // tiles pw, pw + 8, ...
+  const int ch0 = (wave >> 3) * (D / 2) + KH * kq;  // this lane's first channel
   const double* qh = qp + (size_t)bh * nqb * D;
   const double* kh = kp + (size_t)bh * nkb * D;
 
-  // row r of base (clamped to the n rows there are), channels KS kq .. KS kq + KS - 1. Rows past
-  // the end only feed scores that are never read: query rows past nqb and key columns past nkb.
-  auto load_run = [&](const double* base, int r, int n, double (&x)[KS]) {
-    const f64x2* src = reinterpret_cast<const f64x2*>(base + (size_t)min(r, n - 1) * D + KS * kq);
+  for (int e = 2 * threadIdx.x; e < FQ * pitch; e += 2 * FW * 64)
+    *reinterpret_cast<f64x2*>(s_lds + e) = (f64x2){0.0, 0.0};
+
+  // row r of base (clamped to the n rows there are), this lane's KH channels. Rows past the end
+  // only feed scores that are never read: query rows past nqb and key columns past nkb.
+  auto load_run = [&](const double* base, int r, int n, double (&x)[KH]) {
+    const f64x2* src = reinterpret_cast<const f64x2*>(base + (size_t)min(r, n - 1) * D + ch0);
 #pragma unroll
-    for (int s = 0; s < KS / 2; ++s) {
+    for (int s = 0; s < KH / 2; ++s) {
       const f64x2 w = src[s];
       x[2 * s] = w[0];
       x[2 * s + 1] = w[1];
     }
   };
-  double a[KS];
+  double a[KH];
   load_run(qh, i0 + m, nqb, a);
+  __syncthreads();  // the zeroed scores
 
-  // tile t: scores of the group's rows against key blocks 16 t .. 16 t + 15, into LDS
-  auto tile = [&](int t, const double (&b)[KS]) {
+  // tile t: this half's part of the scores of the group's rows against key blocks 16 t .. + 15
+  auto tile = [&](int t, const double (&b)[KH]) {
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
 #pragma unroll
-    for (int s = 0; s < KS; s += 2) {
+    for (int s = 0; s < KH; s += 2) {
       acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], b[s + 1], acc1, 0, 0, 0);
     }
     // result element i: row 4 i + kq, column 16 t + m
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_lds[(4 * i + kq) * pitch + 16 * t + m] = scale * (acc0[i] + acc1[i]);
+    for (int i = 0; i < 4; ++i)
+      __hip_atomic_fetch_add(&s_lds[(4 * i + kq) * pitch + 16 * t + m], scale * (acc0[i] + acc1[i]),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
-  // the wave's tiles t = wave, wave + FW, ...: the next tile's loads (clamped to the last tile, so
-  // that the loop body has no branch) are issued before the current tile's products and moved into
-  // place after them, so the products never wait for the loads in flight.
+  // the next tile's loads (clamped to the last tile, so that the loop body has no branch) are
+  // issued before the current tile's products and moved into place after them, so the products
+  // never wait for the loads in flight
   const int ntile = (nkb + 15) / 16;
-  double bc[KS], bn[KS];
-  load_run(kh, 16 * min(wave, ntile - 1) + m, nkb, bc);
-  for (int t = wave; t < ntile; t += FW) {
-    load_run(kh, 16 * min(t + FW, ntile - 1) + m, nkb, bn);
+  double bc[KH], bn[KH];
+  load_run(kh, 16 * min(pw, ntile - 1) + m, nkb, bc);
+  for (int t = pw; t < ntile; t += 8) {
+    load_run(kh, 16 * min(t + 8, ntile - 1) + m, nkb, bn);
     __builtin_amdgcn_sched_barrier(0);  // the loads go out ahead of the products
     tile(t, bc);
     __builtin_amdgcn_sched_barrier(0);  // and the moves, which wait for them, come after
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bc[s] = bn[s];
+    for (int s = 0; s < KH; ++s) bc[s] = bn[s];
   }
   __syncthreads();
 
-  for (int rr = wave; rr < FQ; rr += FW) {
-    const int row = i0 + rr;
-    if (row >= nqb) break;
-    double* srow = s_lds + (size_t)rr * pitch;
-    double v[R];
+  const int row = i0 + wave;
+  if (row >= nqb) return;  // nothing below synchronises the workgroup
+  double* srow = s_lds + (size_t)wave * pitch;
+  double v[R];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int j = 64 * u + lane;
-      v[u] = j < nkb ? srow[j] : -INFINITY;
-    }
-    // the row's LDS becomes the wave's scratch once every lane has read it
-    wave_sync();
-    const size_t g = (size_t)bh * nqb + row;
-    select_row<R>(v, nkb, k, p, nullptr, mask + g * nkb,
-                  kept_idx ? kept_idx + g * nkb : nullptr, kept_idx ? kept_cnt + g : nullptr,
-                  reinterpret_cast<int64_t*>(srow), srow + 64);
-    wave_sync();
+  for (int u = 0; u < R; ++u) {
+    const int j = 64 * u + lane;
+    v[u] = j < nkb ? srow[j] : -INFINITY;
   }
+  // the row's LDS becomes the wave's scratch once every lane has read it
+  wave_sync();
+  const size_t g = (size_t)bh * nqb + row;
+  select_row<R>(v, nkb, k, p, probs ? probs + g * nkb : nullptr, mask + g * nkb,
+                kept_idx ? kept_idx + g * nkb : nullptr, kept_idx ? kept_cnt + g : nullptr,
+                reinterpret_cast<int64_t*>(srow), srow + 64);
 }
 
 template <int D, int R>
 hipError_t launch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
-                        uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+                        double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
   const int pitch = fused_pitch(nkb);
   const size_t lds = (size_t)FQ * pitch * sizeof(double);
   const auto fn = reinterpret_cast<const void*>(&select_fused_kernel<D, R>);
@@ -734,15 +742,15 @@ hipError_t launch_fused(const double* qp, const double* kp, int BH, int nqb, int
   }
   const int n_items = BH * ((nqb + FQ - 1) / FQ);
   hipLaunchKernelGGL((select_fused_kernel<D, R>), dim3((unsigned)n_items), dim3(FW * 64), lds, stream, qp, kp,
-                     n_items, nqb, nkb, pitch, scale, k, p, mask, kept_idx, kept_cnt);
+                     n_items, nqb, nkb, pitch, scale, k, p, probs, mask, kept_idx, kept_cnt);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
-                          uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+                          double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
   const int r = (nkb + 63) / 64;
-#define SA_FUSED(RR) return launch_fused<D, RR>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream)
+#define SA_FUSED(RR) return launch_fused<D, RR>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream)
   if (r <= 1) SA_FUSED(1);
   if (r <= 2) SA_FUSED(2);
   if (r <= 4) SA_FUSED(4);
@@ -776,11 +784,11 @@ hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, in
                          hipStream_t stream) {
   // Without probs the scores stay on chip (rows of at most FUSED_NKB entries, which the host
   // checks ensure). With probs the scores pass through it: the two kernels together are faster
-  // than the fused one, whose row phase has only eight waves per CU to hide its latency.
+  // than the fused one at 720p, whose groups of 16 rows read each head's Kbar 37 times over.
   if (probs == nullptr) {
     if (nkb > FUSED_NKB) return hipErrorInvalidValue;
-    if (d == 128) return dispatch_fused<128>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
-    return dispatch_fused<64>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
+    if (d == 128) return dispatch_fused<128>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream);
+    return dispatch_fused<64>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream);
   }
   const int tpc = scores_tiles_per_chunk(BH, nqb, nkb);
   const int ntile = (nkb + SK - 1) / SK;
