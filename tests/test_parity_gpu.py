@@ -186,6 +186,7 @@ def test_uniform_rows_keep_lowest_indices():
     assert torch.all(sel["probs"] == 1.0 / 16).item()
     m = sel["mask"].cpu().numpy()[0, 0]
     assert (m[:, :10] == 1).all() and (m[:, 10:] == 0).all()
+    check_no_probs(qp, kp, 0.25, 0.6, sel, False)
 
 
 def test_repeatable_bitwise():
@@ -243,6 +244,7 @@ def test_density_sweep(k_frac):
     m = sel["mask"]
     want = oracle.topk_count(k_frac, m.shape[-1])
     assert torch.all(m.sum(-1, dtype=torch.int64) == want).item()
+    check_no_probs(qp, kp, k_frac, 0.0, sel, False)  # Top-k alone (p = 0) on the probs-free kernel
     check_attention(q, k, v, m, w.bq, w.bk, blocks=sample_blocks(w, x, [3, 30], per_head_random=2, seed=1))
 
 
