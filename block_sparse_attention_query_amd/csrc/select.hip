@@ -626,8 +626,9 @@ __global__ __launch_bounds__(256) void select_rows_kernel(double* __restrict__ p
 
 // For callers that do not want the probabilities. One workgroup per group of FQ query-block rows
 // of a head: the scores of the whole group stay in LDS, so they never make a round trip through
-// HBM. 16 waves, so that the row phase has a wave per row. Phase 1: the group's FQ x nkb scores on the float64 matrix cores. Waves w and w + 8
-// compute the same 16-column tiles t = w mod 8, + 8, ..., over the first and the second half of
+// HBM. 16 waves, so that the row phase has a wave per row. Phase 1: the group's FQ x nkb scores
+// on the float64 matrix cores. Waves w and w + 8 compute the same 16-column tiles
+// t = w mod 8, + 8, ..., over the first and the second half of
 // the channels, and add their partial scores into the zeroed LDS rows (two float64 adds onto
 // zero, so the sum does not depend on their order). Each wave keeps its half of the group's Qbar
 // rows as A operands in registers and reads each tile's Kbar half-rows as B operands straight
