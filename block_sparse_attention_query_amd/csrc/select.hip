@@ -648,8 +648,7 @@ template <int D, int R>
 __global__ __launch_bounds__(FW * 64, 1) void select_fused_kernel(const double* __restrict__ qp,
                                                                   const double* __restrict__ kp, int n_items,
                                                                   int nqb, int nkb, int pitch, double scale, int k,
-                                                                  double p, double* __restrict__ probs,
-                                                                  uint8_t* __restrict__ mask,
+                                                                  double p, uint8_t* __restrict__ mask,
                                                                   int32_t* __restrict__ kept_idx,
                                                                   int32_t* __restrict__ kept_cnt) {
   constexpr int KH = D / 8;  // product steps per channel half
@@ -726,14 +725,14 @@ __global__ __launch_bounds__(FW * 64, 1) void select_fused_kernel(const double* 
   // the row's LDS becomes the wave's scratch once every lane has read it
   wave_sync();
   const size_t g = (size_t)bh * nqb + row;
-  select_row<R>(v, nkb, k, p, probs ? probs + g * nkb : nullptr, mask + g * nkb,
+  select_row<R>(v, nkb, k, p, nullptr, mask + g * nkb,
                 kept_idx ? kept_idx + g * nkb : nullptr, kept_idx ? kept_cnt + g : nullptr,
                 reinterpret_cast<int64_t*>(srow), srow + 64);
 }
 
 template <int D, int R>
 hipError_t launch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
-                        double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+                        uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
   const int pitch = fused_pitch(nkb);
   const size_t lds = (size_t)FQ * pitch * sizeof(double);
   const auto fn = reinterpret_cast<const void*>(&select_fused_kernel<D, R>);
@@ -743,15 +742,15 @@ hipError_t launch_fused(const double* qp, const double* kp, int BH, int nqb, int
   }
   const int n_items = BH * ((nqb + FQ - 1) / FQ);
   hipLaunchKernelGGL((select_fused_kernel<D, R>), dim3((unsigned)n_items), dim3(FW * 64), lds, stream, qp, kp,
-                     n_items, nqb, nkb, pitch, scale, k, p, probs, mask, kept_idx, kept_cnt);
+                     n_items, nqb, nkb, pitch, scale, k, p, mask, kept_idx, kept_cnt);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch_fused(const double* qp, const double* kp, int BH, int nqb, int nkb, double scale, int k, double p,
-                          double* probs, uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
+                          uint8_t* mask, int32_t* kept_idx, int32_t* kept_cnt, hipStream_t stream) {
   const int r = (nkb + 63) / 64;
-#define SA_FUSED(RR) return launch_fused<D, RR>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream)
+#define SA_FUSED(RR) return launch_fused<D, RR>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream)
   if (r <= 1) SA_FUSED(1);
   if (r <= 2) SA_FUSED(2);
   if (r <= 4) SA_FUSED(4);
@@ -788,8 +787,8 @@ hipError_t launch_select(const double* qp, const double* kp, int BH, int nqb, in
   // than the fused one at 720p, whose groups of 16 rows read each head's Kbar 37 times over.
   if (probs == nullptr) {
     if (nkb > FUSED_NKB) return hipErrorInvalidValue;
-    if (d == 128) return dispatch_fused<128>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream);
-    return dispatch_fused<64>(qp, kp, BH, nqb, nkb, scale, k, p, probs, mask, kept_idx, kept_cnt, stream);
+    if (d == 128) return dispatch_fused<128>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
+    return dispatch_fused<64>(qp, kp, BH, nqb, nkb, scale, k, p, mask, kept_idx, kept_cnt, stream);
   }
   const int tpc = scores_tiles_per_chunk(BH, nqb, nkb);
   const int ntile = (nkb + SK - 1) / SK;
