@@ -42,9 +42,14 @@ def attn_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+TRAFFIC_WORKLOAD = "wan720p"  # the workload the committed counters were taken on
+
+
+def measured_traffic(workload: str):
     """HBM bytes per attention launch and its L2 hit rate, from committed rocprofv3 counters, if
-    they were taken on the current kernel source."""
+    they were taken on the current kernel source and on this workload."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None, None
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -622,7 +627,7 @@ def main(argv=None):
 
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     alg_bytes = 4 * B * H * N * d * q.element_size()  # Q, K, V read once and O written once
-    traffic, l2_hit = measured_traffic()
+    traffic, l2_hit = measured_traffic(args.workload)
     result = {
         "metric": "sparse attention fwd TFLOP/s (executed) + ms/call at 95% sparsity; % bf16 MFMA peak",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
