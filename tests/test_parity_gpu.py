@@ -285,6 +285,26 @@ def test_lists_out_of_range_entries_are_clamped(dt):
     assert torch.equal(o[0, 1, 3 * bq:4 * bq], torch.zeros_like(o[0, 1, 3 * bq:4 * bq]))  # count -4 -> empty row
 
 
+@pytest.mark.parametrize("H,nqb,nkb,d", [(7, 40, 300, 128), (3, 17, 1182, 64), (9, 33, 77, 128)])
+def test_select_without_probs_on_uneven_groups(H, nqb, nkb, d):
+    """The probs-free kernel takes 16 query-block rows per workgroup and hands the (head, group)
+    items to the XCDs in contiguous ranges: item counts that are not a multiple of 8 (21, 6, 27)
+    and a ragged last group must still select every row exactly once, as the two-kernel path and
+    the oracle do."""
+    g = torch.Generator().manual_seed(H * 1000 + nqb)
+    base = torch.randn(1, H, 1, d, generator=g, dtype=torch.float64)
+    qp = base + 0.5 * torch.randn(1, H, nqb, d, generator=g, dtype=torch.float64)
+    kp = 0.4 * torch.randn(1, H, nkb, d, generator=g, dtype=torch.float64) + 0.6 * base
+    qp, kp = qp.to(DEV), kp.to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    sel = sa.select_mask(qp, kp, 0.05, 0.9, scale, kept_lists=True)
+    probs = oracle.pooled_probabilities(f64(qp), f64(kp), scale)
+    ref, _ = oracle.select_mask(probs, 0.05, 0.9)
+    rep = oracle.compare_masks(probs, ref, sel["mask"].cpu().numpy(), 0.05, 0.9)
+    assert rep["mismatches"] == 0, rep["mismatch_rows"][:10]
+    check_no_probs(qp, kp, 0.05, 0.9, sel, True, scale)
+
+
 @pytest.mark.parametrize("nkb,k_frac,p", [(1280, 0.03, 0.9), (1281, 0.03, 0.9), (2048, 0.03, 0.9),
                                           (2049, 0.03, 0.9), (3000, 0.1, 0.5),
                                           (8192, 0.01, 0.95)])
